@@ -1,0 +1,196 @@
+"""Dynamic Bifocal RoPE attention (Jet-Long) for MI355X: Python binding of libbifocal.so.
+
+Thin ctypes layer over the C ABI declared in include/bifocal.h: it checks tensor
+dtypes/devices, allocates outputs with torch, and passes raw device pointers and the
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback path.  If the shared library is missing, importing
+this package succeeds but the first call raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "lib", "lib_path", "rope_apply", "bifocal_prefill", "bifocal_decode", "workspace_bytes",
+    "group_size", "Workspace", "BifocalError", "OP_PREFILL", "OP_DECODE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libbifocal.so")
+
+OP_ROPE, OP_PREFILL, OP_DECODE = 0, 1, 2
+_F32, _BF16 = 0, 1
+
+
+class BifocalError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is missing: build it with `python -m dynamic_rope_context_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    vp, i32, i64, sz, f32, f64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_size_t, ctypes.c_float, ctypes.c_double)
+    lib.rope_apply.argtypes = [vp, vp, i32, i32, i32, i32, f64, i32, i32, vp]
+    lib.rope_apply.restype = i32
+    lib.bifocal_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64,
+                                    f32, i32, vp, sz, vp]
+    lib.bifocal_prefill.restype = i32
+    lib.bifocal_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f32,
+                                   i32, vp, sz, vp]
+    lib.bifocal_decode.restype = i32
+    lib.bifocal_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.bifocal_workspace_bytes.restype = sz
+    lib.bifocal_status_string.argtypes = [i32]
+    lib.bifocal_status_string.restype = ctypes.c_char_p
+    lib.bifocal_group_size.argtypes = [i64, i32]
+    lib.bifocal_group_size.restype = i32
+    return lib
+
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded libbifocal.so (loaded on first use; raises if it was not built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise BifocalError(f"{what}: {lib().bifocal_status_string(status).decode()} ({status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise BifocalError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise BifocalError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise BifocalError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def group_size(L: int, w_pretrained: int) -> int:
+    """G = max(1, ceil(L / w_pretrained)) as the kernels compute it."""
+    return int(lib().bifocal_group_size(int(L), int(w_pretrained)))
+
+
+def workspace_bytes(op: int, max_len: int, Hq: int, Hkv: int, D: int) -> int:
+    return int(lib().bifocal_workspace_bytes(op, max_len, Hq, Hkv, D))
+
+
+class Workspace:
+    """Caller-owned device workspace (zero-filled so that it starts with no table)."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        if nbytes <= 0:
+            raise BifocalError("workspace size must be positive")
+        self.buf = torch.zeros(int(nbytes) + 256, dtype=torch.uint8, device=device)
+        off = (-self.buf.data_ptr()) % 256
+        self.ptr = self.buf.data_ptr() + off
+        self.nbytes = int(nbytes)
+
+    @classmethod
+    def for_op(cls, op: int, max_len: int, Hq: int, Hkv: int, D: int, device="cuda"):
+        n = workspace_bytes(op, max_len, Hq, Hkv, D)
+        if n == 0:
+            raise BifocalError("invalid workspace request")
+        return cls(n, device)
+
+
+def rope_apply(x: torch.Tensor, theta: float, pos: Optional[torch.Tensor] = None, pos0: int = 0,
+               G: int = 1, stream=None) -> torch.Tensor:
+    """In place: x[t, h, :] <- R(floor(p_t / G)) x[t, h, :] (G = 1: standard RoPE)."""
+    if x.dim() != 3:
+        raise BifocalError("x must be [T, H, D]")
+    T, H, D = x.shape
+    pp = 0
+    if pos is not None:
+        if pos.dtype != torch.int32 or pos.numel() != T:
+            raise BifocalError("pos must be int32 [T]")
+        pp = _dev(pos, "pos")
+    _check(lib().rope_apply(_dev(x, "x"), pp, int(pos0), T, H, D, float(theta), int(G),
+                           _dtype_code(x), _stream(stream)), "rope_apply")
+    return x
+
+
+def bifocal_prefill(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                    cu_seqlens: Sequence[int], w0: int, w_pretrained: int, theta: float,
+                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                    workspace: Optional[Workspace] = None, stream=None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Bifocal causal attention over packed sequences.  Q [T,Hq,D], K/V [T,Hkv,D] carry
+    standard RoPE at local positions.  Returns (O [T,Hq,D], LSE [Hq,T] float32 or None)."""
+    if Q.dim() != 3 or K.dim() != 3 or V.shape != K.shape:
+        raise BifocalError("expected Q [T,Hq,D], K and V [T,Hkv,D]")
+    T, Hq, D = Q.shape
+    Hkv = K.shape[1]
+    if K.shape[0] != T or K.shape[2] != D or K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise BifocalError("Q, K, V shapes or dtypes disagree")
+    cu = [int(c) for c in cu_seqlens]
+    B = len(cu) - 1
+    cu_arr = (ctypes.c_int32 * len(cu))(*cu)
+    if out is None:
+        out = torch.empty_like(Q)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        max_len = max([cu[b + 1] - cu[b] for b in range(B)] + [0])
+        workspace = Workspace.for_op(OP_PREFILL, max(max_len, 1), Hq, Hkv, D, Q.device)
+    _check(lib().bifocal_prefill(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else 0,
+        ctypes.cast(cu_arr, ctypes.c_void_p), B, Hq, Hkv, D, int(w0), int(w_pretrained),
+        float(theta), float(softmax_scale), _dtype_code(Q), workspace.ptr, workspace.nbytes,
+        _stream(stream)), "bifocal_prefill")
+    return out, lse
+
+
+def bifocal_decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, pos: int,
+                   w0: int, w_pretrained: int, theta: float, softmax_scale: float = 0.0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   want_lse: bool = True, workspace: Optional[Workspace] = None, stream=None
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One decode step: q [Hq,D] at position pos over cache entries 0..pos of
+    Kcache/Vcache [S,Hkv,D] (standard RoPE).  Returns (o [Hq,D], LSE [Hq] or None)."""
+    if q.dim() != 2 or Kcache.dim() != 3 or Vcache.shape != Kcache.shape:
+        raise BifocalError("expected q [Hq,D], Kcache and Vcache [S,Hkv,D]")
+    Hq, D = q.shape
+    S, Hkv = Kcache.shape[0], Kcache.shape[1]
+    if pos + 1 > S:
+        raise BifocalError("the cache holds fewer than pos + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = Workspace.for_op(OP_DECODE, pos + 1, Hq, Hkv, D, q.device)
+    _check(lib().bifocal_decode(
+        _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else 0, int(pos), Hq, Hkv, D, int(w0),
+        int(w_pretrained), float(theta), float(softmax_scale), _dtype_code(q), workspace.ptr,
+        workspace.nbytes, _stream(stream)), "bifocal_decode")
+    return out, lse

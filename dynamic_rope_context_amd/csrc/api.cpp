@@ -1,0 +1,266 @@
+// C ABI of the bifocal RoPE attention library: argument validation, workspace
+// layout, per-sequence group size, and kernel dispatch on the caller's stream.
+// Every argument check happens before the first enqueue, so an error leaves all
+// buffers untouched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "bf_common.h"
+#include "prefill_args.h"
+#include "decode_args.h"
+
+extern "C" {
+#include "../../include/bifocal.h"
+}
+
+namespace bifocal {
+hipError_t launch_table_ensure(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
+                               bool full, uint32_t token, hipStream_t stream);
+hipError_t launch_rope_apply(void* x, const int32_t* pos, int pos0, int T_, int H, int D,
+                             double theta, int G, bool bf16, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& args, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillArgs& args, hipStream_t stream);
+hipError_t launch_pair_select(const void* Q, const void* K, int T, int Hq, int Hkv,
+                              uint32_t* mx, int32_t* sel, hipStream_t stream);
+int prefill_f32_rows_per_block();
+int prefill_mfma_positions_per_block(int rep);
+
+hipError_t launch_decode(const DecodeArgs& a, int rep, int D, bool bf16, hipStream_t stream);
+}  // namespace bifocal
+
+using namespace bifocal;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t group_size(int64_t L, int32_t w_pre) {
+  if (L < 0 || w_pre < 1) return 0;
+  const int64_t G = (L + w_pre - 1) / w_pre;
+  return (int32_t)std::max<int64_t>(1, G);
+}
+
+// Host-side memory of which workspaces already hold a table.  Only a hint for the
+// launch size of the table check: the device header decides validity.
+struct TableHint {
+  const void* ws;
+  double theta;
+  int D;
+  int n_valid;
+};
+std::mutex g_hint_mu;
+std::vector<TableHint> g_hints;
+std::atomic<uint32_t> g_token{0};
+
+uint32_t next_token() {
+  static const uint32_t seed = (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  uint32_t t = seed ^ (0x9e3779b9u * (g_token.fetch_add(1) + 1));
+  return t ? t : 1u;
+}
+
+bf_status ensure_table(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
+                       hipStream_t stream) {
+  bool believed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_hint_mu);
+    for (auto& h : g_hints)
+      if (h.ws == ws && h.theta == theta && h.D == D && h.n_valid >= n_needed) believed = true;
+  }
+  hipError_t e = launch_table_ensure(ws, lay, D, theta, n_needed, !believed, next_token(), stream);
+  if (e != hipSuccess) return BF_EHIP;
+  if (!believed) {
+    const long long want = ((long long)n_needed + 65535) / 65536 * 65536;
+    const int n_build = (int)std::min<long long>(want, lay.n_cap);
+    std::lock_guard<std::mutex> lk(g_hint_mu);
+    g_hints.erase(std::remove_if(g_hints.begin(), g_hints.end(),
+                                 [&](const TableHint& h) { return h.ws == ws; }),
+                  g_hints.end());
+    if (g_hints.size() >= 64) g_hints.erase(g_hints.begin());
+    g_hints.push_back(TableHint{ws, theta, D, n_build});
+  } else {
+    std::lock_guard<std::mutex> lk(g_hint_mu);
+    for (auto& h : g_hints)
+      if (h.ws == ws) h.n_valid = std::min(h.n_valid, lay.n_cap);
+  }
+  return BF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bifocal_status_string(int32_t s) {
+  switch (s) {
+    case BF_OK: return "ok";
+    case BF_EINVAL: return "invalid argument";
+    case BF_EUNSUPPORTED: return "unsupported configuration";
+    case BF_EWORKSPACE: return "workspace missing or too small";
+    case BF_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t bifocal_group_size(int64_t L, int32_t w_pretrained) { return group_size(L, w_pretrained); }
+
+size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (op < 0 || op > 2 || max_len < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || (D != 64 && D != 128))
+    return 0;
+  if (op == BF_OP_ROPE) return 0;
+  return ws_bytes_for(op, max_len, Hq, Hkv, D);
+}
+
+bf_status rope_apply(void* x, const int32_t* pos, int32_t pos0, int32_t T, int32_t H, int32_t D,
+                     double theta, int32_t G, bf_dtype dt, bf_stream stream) {
+  if (T < 0 || H < 1 || D < 2 || (D & 1) || G < 1 || !(theta > 0.0) || !std::isfinite(theta))
+    return BF_EINVAL;
+  if (dt != BF_F32 && dt != BF_BF16) return BF_EINVAL;
+  if (D > 256) return BF_EUNSUPPORTED;
+  if (T == 0) return BF_OK;
+  if (!x) return BF_EINVAL;
+  if (!pos && (pos0 < 0 || (int64_t)pos0 + T - 1 > INT32_MAX)) return BF_EINVAL;
+  if (!aligned(x, dt == BF_BF16 ? 2 : 4) || (pos && !aligned(pos, 4))) return BF_EINVAL;
+  hipError_t e = launch_rope_apply(x, pos, pos0, T, H, D, theta, G, dt == BF_BF16,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? BF_OK : BF_EHIP;
+}
+
+bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, float* lse,
+                          const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t w0, int32_t w_pretrained, double theta,
+                          float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
+                          bf_stream stream) {
+  if (!cu_seqlens || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 1 || w_pretrained < 1 ||
+      !(theta > 0.0) || !std::isfinite(theta) || !std::isfinite(softmax_scale))
+    return BF_EINVAL;
+  if (dt != BF_F32 && dt != BF_BF16) return BF_EINVAL;
+  if (cu_seqlens[0] != 0) return BF_EINVAL;
+  int32_t max_len = 0;
+  for (int b = 0; b < B; ++b) {
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return BF_EINVAL;
+    max_len = std::max(max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
+  }
+  const int32_t T = cu_seqlens[B];
+  if (D != 64 && D != 128) return BF_EUNSUPPORTED;
+  const int rep = Hq / Hkv;
+  if (dt == BF_BF16 && (D != 128 || (rep != 1 && rep != 2 && rep != 4 && rep != 8)))
+    return BF_EUNSUPPORTED;
+  if (T == 0) return BF_OK;
+  if (!Q || !K || !V || !O) return BF_EINVAL;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      (lse && !aligned(lse, 4)))
+    return BF_EINVAL;
+  if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
+  const WsLayout lay = ws_layout(BF_OP_PREFILL, Hq, Hkv, D, ws_bytes);
+  if (lay.scratch_off == 0 || lay.n_cap < max_len) return BF_EWORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  bf_status s = ensure_table(ws, lay, D, theta, max_len, st);
+  if (s != BF_OK) return s;
+
+  char* wsb = reinterpret_cast<char*>(ws);
+  uint32_t* mx = reinterpret_cast<uint32_t*>(wsb + lay.scratch_off);
+  int32_t* sel = reinterpret_cast<int32_t*>(
+      wsb + lay.scratch_off + align_up((size_t)(Hq + Hkv) * 64 * sizeof(uint32_t), 256));
+  if (dt == BF_BF16) {
+    if (launch_pair_select(Q, K, T, Hq, Hkv, mx, sel, st) != hipSuccess) return BF_EHIP;
+  }
+
+  PrefillArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.lse = lse;
+  a.tab = reinterpret_cast<const float2*>(wsb + lay.table_off);
+  a.sel = sel;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.w0 = w0;
+  a.scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  const int rows = dt == BF_BF16 ? prefill_mfma_positions_per_block(rep)
+                                 : prefill_f32_rows_per_block();
+  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
+    int n = 0, maxq = 0;
+    for (int b = b0; b < std::min(B, b0 + kMaxSeqPerLaunch); ++b) {
+      const int L = cu_seqlens[b + 1] - cu_seqlens[b];
+      if (L == 0) continue;
+      a.seq[n].start = cu_seqlens[b];
+      a.seq[n].len = L;
+      a.seq[n].G = group_size(L, w_pretrained);
+      maxq = std::max(maxq, (L + rows - 1) / rows);
+      ++n;
+    }
+    if (n == 0) continue;
+    a.nseq = n;
+    a.max_qblocks = maxq;
+    hipError_t e = dt == BF_BF16 ? launch_prefill_mfma(a, st) : launch_prefill_f32(a, st);
+    if (e != hipSuccess) return BF_EHIP;
+  }
+  return BF_OK;
+}
+
+bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, void* o,
+                         float* lse, int32_t pos, int32_t Hq, int32_t Hkv, int32_t D, int32_t w0,
+                         int32_t w_pretrained, double theta, float softmax_scale, bf_dtype dt,
+                         void* ws, size_t ws_bytes, bf_stream stream) {
+  if (!q || !Kcache || !Vcache || !o || pos < 0 || pos == INT32_MAX || Hq < 1 || Hkv < 1 ||
+      Hq % Hkv || w0 < 1 || w_pretrained < 1 || !(theta > 0.0) || !std::isfinite(theta) ||
+      !std::isfinite(softmax_scale))
+    return BF_EINVAL;
+  if (dt != BF_F32 && dt != BF_BF16) return BF_EINVAL;
+  if (D != 64 && D != 128) return BF_EUNSUPPORTED;
+  const int rep = Hq / Hkv;
+  if (rep != 1 && rep != 2 && rep != 4 && rep != 8) return BF_EUNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(Kcache, 16) || !aligned(Vcache, 16) ||
+      !aligned(o, dt == BF_BF16 ? 2 : 4) || (lse && !aligned(lse, 4)))
+    return BF_EINVAL;
+  if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
+  const WsLayout lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes);
+  const int32_t n_keys = pos + 1;
+  if (lay.scratch_off == 0 || lay.n_cap < n_keys) return BF_EWORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  bf_status s = ensure_table(ws, lay, D, theta, n_keys, st);
+  if (s != BF_OK) return s;
+
+  // Split the cache so that ~2048 workgroups stream it; splits are whole multiples of
+  // 64 keys and their count a multiple of 8 (one slice per XCD).
+  int nsplit = (2048 + Hkv - 1) / Hkv;
+  nsplit = std::min(kDecodeMaxSplits, std::max(8, (nsplit + 7) / 8 * 8));
+  int kps = (n_keys + nsplit - 1) / nsplit;
+  kps = (kps + 63) / 64 * 64;
+  nsplit = (n_keys + kps - 1) / kps;
+  nsplit = (nsplit + 7) / 8 * 8;
+  if (nsplit > kDecodeMaxSplits) return BF_EUNSUPPORTED;
+
+  char* wsb = reinterpret_cast<char*>(ws);
+  DecodeArgs a{};
+  a.q = q;
+  a.K = Kcache;
+  a.V = Vcache;
+  a.tab = reinterpret_cast<const float2*>(wsb + lay.table_off);
+  a.part = reinterpret_cast<float*>(wsb + lay.scratch_off);
+  a.o = o;
+  a.lse = lse;
+  a.pos = pos;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.w0 = w0;
+  a.G = group_size((int64_t)pos + 1, w_pretrained);
+  a.nsplit = nsplit;
+  a.kps = kps;
+  const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt((double)D);
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  hipError_t e = launch_decode(a, rep, D, dt == BF_BF16, st);
+  return e == hipSuccess ? BF_OK : BF_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Shared device/host definitions for the bifocal RoPE attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bifocal {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Position table kept in the workspace.
+//
+// tab[p][m] = (cos(p * theta_m), sin(p * theta_m)) for p in [0, n_valid), float32
+// values rounded once from float64.  It serves both branches' needs:
+//   * standard RoPE at position p,
+//   * the correction rotation of the remote branch, R(f(x) - x) = R(-(x - f(x))),
+//     read at n = x - f(x) with the sine negated.  Indexing by n rather than by x
+//     keeps the table independent of G, so one table serves every sequence of a
+//     ragged batch and every decode step (RoPE rotations compose additively; the
+//     pages' on-the-fly correction rotation, technical summary section 2).
+// ---------------------------------------------------------------------------
+struct TableHeader {
+  uint64_t magic;      // kTableMagic once a table is complete
+  double theta;
+  int32_t D;
+  int32_t n_valid;     // positions covered
+  uint64_t done;       // builder blocks finished, tagged with the build's token
+  uint32_t pad[56];
+};
+static_assert(sizeof(TableHeader) == 256, "header is one 256-byte slot");
+
+constexpr uint64_t kTableMagic = 0x42464f43414c5442ull;  // "BTLACOFB"
+
+// Workspace layout: [header 256 B][table rows 0 .. n_cap-1][op scratch at the end].
+// The table offset does not depend on the operation, so prefill and decode calls can
+// share one workspace and its table.
+struct WsLayout {
+  size_t table_off, scratch_off, scratch_bytes;
+  int32_t n_cap;  // positions the table region can hold
+};
+
+constexpr int kDecodeMaxSplits = 512;
+constexpr int kSelPairs = 4;  // RoPE pairs per KV head given the hi/lo correction
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline size_t table_row_bytes(int D) { return (size_t)(D / 2) * 2 * sizeof(float); }
+
+// Op scratch: decode partials, or prefill pair maxima + selected pairs.
+inline size_t scratch_bytes(int op, int Hq, int Hkv, int D) {
+  if (op == 2) return align_up((size_t)Hq * kDecodeMaxSplits * (D + 2) * sizeof(float), 256);
+  if (op == 1) {
+    const size_t mx = align_up((size_t)(Hq + Hkv) * 64 * sizeof(uint32_t), 256);
+    return mx + align_up((size_t)Hkv * kSelPairs * sizeof(int32_t), 256);
+  }
+  return 0;
+}
+
+inline WsLayout ws_layout(int op, int Hq, int Hkv, int D, size_t ws_bytes) {
+  WsLayout l;
+  l.table_off = 256;
+  l.scratch_bytes = scratch_bytes(op, Hq, Hkv, D);
+  const size_t ws = ws_bytes / 256 * 256;
+  l.scratch_off = ws > l.scratch_bytes ? ws - l.scratch_bytes : 0;
+  const size_t room = l.scratch_off > l.table_off ? l.scratch_off - l.table_off : 0;
+  const size_t n = room / table_row_bytes(D);
+  l.n_cap = n > (size_t)INT32_MAX ? INT32_MAX : (int32_t)n;
+  return l;
+}
+
+inline size_t ws_bytes_for(int op, int max_len, int Hq, int Hkv, int D) {
+  return 256 + align_up((size_t)max_len * table_row_bytes(D), 256) +
+         scratch_bytes(op, Hq, Hkv, D);
+}
+
+// ---------------------------------------------------------------------------
+// Scalar helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// theta_m = theta^(-2m/D) and the angle p * theta_m in float64.
+__device__ __forceinline__ double inv_freq64(double theta, int m, int D) {
+  return pow(theta, -2.0 * (double)m / (double)D);
+}
+
+// f(x) = floor(x / G) and n(x) = x - f(x) for x >= 0.
+__device__ __forceinline__ int alias_pos(int x, int G) { return x / G; }
+
+}  // namespace bifocal

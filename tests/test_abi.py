@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects
+bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bifocal.h")
+LIB = os.path.join(ROOT, "dynamic_rope_context_amd", "libbifocal.so")
+
+BF_OK, BF_EINVAL, BF_EUNSUPPORTED, BF_EWORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\(", text)) - {"defined", "if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libbifocal.so is not built (run __graft_entry__.build())")
+    import dynamic_rope_context_amd as b
+    return b.lib()
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("bifocal_prefill", "bifocal_decode", "rope_apply", "bifocal_workspace_bytes",
+              "bifocal_status_string", "bifocal_group_size"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in bifocal.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.bifocal_status_string(s)
+    assert lib.bifocal_status_string(99) == b"unknown status"
+
+
+def test_group_size_export(lib):
+    assert lib.bifocal_group_size(131072, 32768) == 4
+    assert lib.bifocal_group_size(131073, 32768) == 5
+    assert lib.bifocal_group_size(1, 32768) == 1
+    assert lib.bifocal_group_size(0, 32768) == 1
+    assert lib.bifocal_group_size(98427, 32768) == 4
+    assert lib.bifocal_group_size(40001, 32768) == 2
+    assert lib.bifocal_group_size(-1, 32768) == 0
+    assert lib.bifocal_group_size(5, 0) == 0
+
+
+def test_workspace_bytes(lib):
+    n = lib.bifocal_workspace_bytes(1, 131072, 32, 8, 128)
+    assert n >= 131072 * 64 * 8          # the position table alone
+    assert lib.bifocal_workspace_bytes(2, 131072, 32, 8, 128) > 0
+    assert lib.bifocal_workspace_bytes(1, 10, 3, 2, 128) == 0   # Hq % Hkv != 0
+    assert lib.bifocal_workspace_bytes(1, 10, 4, 2, 96) == 0    # unsupported D
+    assert lib.bifocal_workspace_bytes(7, 10, 4, 2, 128) == 0
+
+
+def _prefill(lib, **kw):
+    args = dict(Q=16, K=16, V=16, O=16, lse=0, cu=None, B=1, Hq=4, Hkv=1, D=128, w0=4,
+                w_pre=16, theta=1e4, scale=0.0, dt=1, ws=256, ws_bytes=1 << 30)
+    args.update(kw)
+    cu = args["cu"] if args["cu"] is not None else [0, 64]
+    cu_ptr = None
+    if cu != 0:
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        cu_ptr = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.bifocal_prefill(args["Q"], args["K"], args["V"], args["O"], args["lse"],
+                               cu_ptr, args["B"], args["Hq"], args["Hkv"], args["D"],
+                               args["w0"], args["w_pre"], args["theta"], args["scale"],
+                               args["dt"], args["ws"], args["ws_bytes"], None)
+
+
+def test_prefill_rejects_bad_arguments_before_launch(lib):
+    # every case returns before any HIP call (the pointers are fake)
+    assert _prefill(lib, w0=0) == BF_EINVAL
+    assert _prefill(lib, w_pre=0) == BF_EINVAL
+    assert _prefill(lib, theta=-1.0) == BF_EINVAL
+    assert _prefill(lib, Hq=3, Hkv=2) == BF_EINVAL
+    assert _prefill(lib, cu=[1, 64]) == BF_EINVAL
+    assert _prefill(lib, cu=[0, 64, 32], B=2) == BF_EINVAL
+    assert _prefill(lib, cu=0) == BF_EINVAL
+    assert _prefill(lib, D=96) == BF_EUNSUPPORTED
+    assert _prefill(lib, D=64) == BF_EUNSUPPORTED           # bf16 path needs D = 128
+    assert _prefill(lib, Hq=12, Hkv=4) == BF_EUNSUPPORTED   # bf16 path: ratio 3
+    assert _prefill(lib, Q=0) == BF_EINVAL
+    assert _prefill(lib, Q=8) == BF_EINVAL                  # misaligned
+    assert _prefill(lib, ws=0) == BF_EWORKSPACE
+    assert _prefill(lib, ws=128) == BF_EWORKSPACE           # misaligned workspace
+    assert _prefill(lib, ws_bytes=4096) == BF_EWORKSPACE
+    assert _prefill(lib, dt=7) == BF_EINVAL
+    assert _prefill(lib, cu=[0, 0], Q=0) == BF_OK           # empty batch: nothing to do
+
+
+def _decode(lib, **kw):
+    a = dict(q=16, K=16, V=16, o=16, lse=0, pos=100, Hq=4, Hkv=1, D=128, w0=4, w_pre=16,
+             theta=1e4, scale=0.0, dt=1, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.bifocal_decode(a["q"], a["K"], a["V"], a["o"], a["lse"], a["pos"], a["Hq"],
+                              a["Hkv"], a["D"], a["w0"], a["w_pre"], a["theta"], a["scale"],
+                              a["dt"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_rejects_bad_arguments_before_launch(lib):
+    assert _decode(lib, pos=-1) == BF_EINVAL
+    assert _decode(lib, q=0) == BF_EINVAL
+    assert _decode(lib, w0=0) == BF_EINVAL
+    assert _decode(lib, Hq=6, Hkv=4) == BF_EINVAL
+    assert _decode(lib, Hq=12, Hkv=4) == BF_EUNSUPPORTED
+    assert _decode(lib, D=80) == BF_EUNSUPPORTED
+    assert _decode(lib, K=24) == BF_EINVAL
+    assert _decode(lib, ws=0) == BF_EWORKSPACE
+    assert _decode(lib, ws_bytes=1 << 12) == BF_EWORKSPACE
+
+
+def test_rope_apply_rejects_bad_arguments(lib):
+    f = lib.rope_apply
+    assert f(16, None, 0, 10, 2, 7, 1e4, 1, 1, None) == BF_EINVAL     # odd D
+    assert f(16, None, 0, 10, 2, 8, 1e4, 0, 1, None) == BF_EINVAL     # G < 1
+    assert f(16, None, 0, 10, 2, 8, 0.0, 1, 1, None) == BF_EINVAL     # theta
+    assert f(None, None, 0, 10, 2, 8, 1e4, 1, 1, None) == BF_EINVAL   # null x
+    assert f(16, None, -1, 10, 2, 8, 1e4, 1, 1, None) == BF_EINVAL    # pos0 < 0
+    assert f(16, None, 0, 10, 2, 512, 1e4, 1, 1, None) == BF_EUNSUPPORTED
+    assert f(16, None, 0, 0, 2, 8, 1e4, 1, 1, None) == BF_OK          # empty
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import dynamic_rope_context_amd as b
+    monkeypatch.setattr(b, "lib_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_lib_handle", None)
+    with pytest.raises(ImportError):
+        b.lib()

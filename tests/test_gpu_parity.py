@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by
+element, on seeded inputs at sizes the oracle finishes in seconds (several tiles,
+ragged tails, every supported GQA ratio, window/group edge cases)."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle.bifocal_ref import (bifocal_decode_ref, bifocal_prefill_ref, group_size,
+                                rope_apply_ref, rope_rotate)
+from helpers import (BF16_TOL, F32_TOL, decode_inputs, errors, prefill_inputs, std_query,
+                     to_dtype, within)
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def bf():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import dynamic_rope_context_amd as m
+    m.lib()  # raises if the library is missing
+    return m
+
+
+def dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(TDT[dt]).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+def run_prefill(bf, w, Q, K, V, cu):
+    O, lse = bf.bifocal_prefill(dev(Q, w.dtype), dev(K, w.dtype), dev(V, w.dtype),
+                                [int(c) for c in cu], w.w0, w.w_pretrained, w.theta)
+    torch.cuda.synchronize()
+    return host(O), lse.cpu().numpy()
+
+
+def check_prefill(bf, w, Q, K, V, cu, tol, rows_per_seq=None):
+    Og, Lg = run_prefill(bf, w, Q, K, V, cu)
+    ref = bifocal_prefill_ref(Q, K, V, cu, w.w0, w.w_pretrained, w.theta,
+                              rows_per_seq=rows_per_seq)
+    worst = {}
+    for b, (rows, O, LSE) in enumerate(ref):
+        if O is None:
+            continue
+        s = int(cu[b])
+        e = errors(Og[s + rows], O, Lg[:, s + rows].T, LSE)
+        say(f"  seq {b}: L={int(cu[b+1]-cu[b])} G={group_size(int(cu[b+1]-cu[b]), w.w_pretrained)}"
+            f" {e}")
+        for k, v in e.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+        assert within(e, tol), (b, e, tol)
+        assert np.all(np.isfinite(Og[s + rows]))
+    return worst
+
+
+# ---------------------------------------------------------------------------
+# rope_apply
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,G,use_pos", [("bf16", 1, False), ("bf16", 3, True),
+                                          ("f32", 1, True), ("f32", 4, False)])
+def test_rope_apply_matches_oracle(bf, dt, G, use_pos):
+    say(f"rope_apply dt={dt} G={G} pos_array={use_pos}")
+    rng = np.random.default_rng(7)
+    T, H, D, theta = 300, 3, 128, 1e6
+    x = to_dtype(rng.standard_normal((T, H, D)).astype(np.float32), dt)
+    pos = rng.integers(0, 131072, size=T).astype(np.int32) if use_pos else None
+    p = pos if use_pos else np.arange(T) + 1000
+    xd = dev(x, dt)
+    bf.rope_apply(xd, theta, pos=torch.from_numpy(pos).cuda() if use_pos else None,
+                  pos0=0 if use_pos else 1000, G=G)
+    torch.cuda.synchronize()
+    got = host(xd).astype(np.float64)
+    exact = rope_apply_ref(x, p, theta, G)
+    if dt == "bf16":
+        # within one bf16 ulp of the exact value (float32 arithmetic, then one rounding)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
+        assert np.all(np.abs(got - exact) <= ulp)
+    else:
+        mag = np.abs(x[..., :D // 2]).max() + np.abs(x[..., D // 2:]).max()
+        assert np.max(np.abs(got - exact)) <= 4e-7 * mag
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def test_prefill_tiny_f32_workload(bf):
+    w = W.get("tiny_f32")
+    say("prefill", w)
+    Q, K, V, cu = prefill_inputs(w)
+    check_prefill(bf, w, Q, K, V, cu, F32_TOL)
+
+
+def test_prefill_f32_ragged_d128(bf):
+    w = W.Workload("f32_ragged", "prefill", "f32", Hq=6, Hkv=2, D=128, w0=50, w_pretrained=64,
+                   theta=1e6, seqlens=(100, 333, 1, 64), outliers=4, seed=77)
+    say("prefill", w)
+    Q, K, V, cu = prefill_inputs(w)
+    check_prefill(bf, w, Q, K, V, cu, F32_TOL)
+
+
+BF16_CASES = [
+    # name, Hq, Hkv, seqlens, w_pretrained, w0, outliers
+    ("rep4_g4", 8, 2, (1000,), 256, 100, 4),
+    ("rep1_ragged", 4, 4, (700, 45, 1333), 300, 64, 0),
+    ("rep2_ragged", 8, 4, (513, 64, 1), 128, 200, 4),
+    ("rep8_w0_1", 16, 2, (777,), 200, 1, 0),
+    ("rep4_g1", 4, 1, (500,), 600, 64, 0),
+    ("rep4_wide_window", 8, 2, (2500,), 512, 1000, 4),
+    ("rep4_w0_ge_L", 4, 1, (300,), 64, 400, 4),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_prefill_bf16_matches_oracle(bf, case):
+    name, Hq, Hkv, seqlens, w_pre, w0, outl = case
+    w = W.Workload(name, "prefill", "bf16", Hq=Hq, Hkv=Hkv, D=128, w0=w0, w_pretrained=w_pre,
+                   theta=1e6, seqlens=seqlens, outliers=outl, seed=900 + len(name))
+    say("prefill", w)
+    Q, K, V, cu = prefill_inputs(w)
+    check_prefill(bf, w, Q, K, V, cu, BF16_TOL)
+
+
+def test_prefill_bf16_aligned_outliers_stress(bf):
+    # the q heads of a group share the KV head's outlier channels: the hi/lo split on
+    # the selected pairs is what keeps the remote scores accurate here
+    w = W.Workload("aligned", "prefill", "bf16", Hq=8, Hkv=2, D=128, w0=64, w_pretrained=512,
+                   theta=1e6, seqlens=(2048,), outliers=0, seed=4242)
+    say("prefill aligned outliers", w)
+    Q, K, V, cu = prefill_inputs(w)
+    rng = np.random.default_rng(5)
+    q, k, v = W.raw_prefill_inputs(w)
+    for g in range(w.Hkv):
+        ch = rng.choice(128, size=4, replace=False)
+        for c in ch:
+            k[:, g, c] *= 8
+            for r in range(4):
+                q[:, g * 4 + r, c] *= 8
+    from helpers import std_rope_local
+    Q = to_dtype(std_rope_local(q, cu, w.theta), "bf16")
+    K = to_dtype(std_rope_local(k, cu, w.theta), "bf16")
+    check_prefill(bf, w, Q, K, V, cu, BF16_TOL)
+
+
+def test_prefill_bf16_g1_is_vanilla_bitwise(bf):
+    # G = 1: every pair uses standard RoPE whatever w0 is, so w0 = 1 and w0 >= L must give
+    # identical bits (same kernel path), and both must match the oracle.
+    w = W.Workload("g1", "prefill", "bf16", Hq=8, Hkv=2, D=128, w0=1, w_pretrained=4096,
+                   theta=1e6, seqlens=(1500,), seed=31)
+    Q, K, V, cu = prefill_inputs(w)
+    O1, L1 = run_prefill(bf, w, Q, K, V, cu)
+    O2, L2 = run_prefill(bf, dataclasses.replace(w, w0=5000), Q, K, V, cu)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    check_prefill(bf, w, Q, K, V, cu, BF16_TOL)
+
+
+def test_prefill_bf16_deterministic(bf):
+    w = W.Workload("det", "prefill", "bf16", Hq=8, Hkv=2, D=128, w0=100, w_pretrained=300,
+                   theta=1e6, seqlens=(900, 333), outliers=4, seed=12)
+    Q, K, V, cu = prefill_inputs(w)
+    O1, L1 = run_prefill(bf, w, Q, K, V, cu)
+    O2, L2 = run_prefill(bf, w, Q, K, V, cu)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_prefill_empty_batch_is_noop(bf):
+    Q = torch.zeros((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros((0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    O, lse = bf.bifocal_prefill(Q, K, K, [0, 0], 4, 16, 1e4)
+    assert O.shape == (0, 4, 128)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,D,Hq,Hkv", [("bf16", 128, 8, 2), ("f32", 128, 4, 4),
+                                         ("bf16", 64, 8, 1), ("f32", 64, 16, 2)])
+def test_decode_matches_oracle(bf, dt, D, Hq, Hkv):
+    w = W.Workload("dec", "decode", dt, Hq=Hq, Hkv=Hkv, D=D, w0=100, w_pretrained=1000,
+                   theta=1e6, cache_len=3000, decode_steps=4, outliers=4, seed=55)
+    say("decode", w)
+    q_raw, Kc, Vc = decode_inputs(w)
+    Kd, Vd = dev(Kc, dt), dev(Vc, dt)
+    ws = bf.Workspace.for_op(bf.OP_DECODE, 3000, Hq, Hkv, D)
+    tol = BF16_TOL if dt == "bf16" else F32_TOL
+    for step, pos in enumerate((0, 5, 99, 100, 999, 1000, 2001, 2999)):
+        q = std_query(q_raw[step % q_raw.shape[0]], pos, w.theta, dt)
+        o, lse = bf.bifocal_decode(dev(q, dt), Kd, Vd, pos, w.w0, w.w_pretrained, w.theta,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        Or, Lr = bifocal_decode_ref(q, Kc, Vc, pos, w.w0, w.w_pretrained, w.theta)
+        e = errors(host(o), Or, lse.cpu().numpy(), Lr)
+        say(f"  pos={pos} G={group_size(pos + 1, w.w_pretrained)} {e}")
+        assert within(e, tol), (pos, e)
+
+
+def test_decode_equals_prefill_last_row(bf):
+    # the cache is read as is: decode at pos equals row pos of a prefill of length pos+1
+    w = W.Workload("cross", "prefill", "bf16", Hq=8, Hkv=2, D=128, w0=64, w_pretrained=256,
+                   theta=1e6, seqlens=(1200,), outliers=4, seed=99)
+    Q, K, V, cu = prefill_inputs(w)
+    for pos in (1199, 700, 255, 256):
+        Og, Lg = run_prefill(bf, dataclasses.replace(w, seqlens=(pos + 1,)), Q[:pos + 1],
+                             K[:pos + 1], V[:pos + 1], [0, pos + 1])
+        o, lse = bf.bifocal_decode(dev(Q[pos], "bf16"), dev(K, "bf16"), dev(V, "bf16"), pos,
+                                   w.w0, w.w_pretrained, w.theta)
+        torch.cuda.synchronize()
+        e = errors(host(o), Og[pos], lse.cpu().numpy(), Lg[:, pos])
+        say(f"  pos={pos} decode vs prefill row: {e}")
+        assert within(e, BF16_TOL)
