@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the bifocal RoPE attention hot path on one MI355X.
+
+A step is one bifocal prefill of the Qwen3-4B-shaped 128K workload (32 query heads,
+8 KV heads, head dim 128, L = 131072, w_pretrained = 32768 so G = 4, w0 = 4096,
+theta = 1e6, outlier channels), inputs resident in HBM.  The same run also times the
+Qwen3-8B-shaped decode workload (256 consecutive steps ending at position 131071 over
+a 128K standard-RoPE cache) and reports it in the "decode" object.
+
+Prints one JSON line on stdout; progress goes to stderr.
+  value      prefill TFLOP/s counted as causal-attention FLOPs plus the second score
+             set over the local window: F = 4*D*Hq*sum_i(i+1) + 2*D*Hq*sum_i min(i+1, w0)
+  roofline   the prefill kernel against the dense bf16 MFMA peak (2500 TFLOP/s)
+  decode     KV GB/s = bytes of K and V read per step / step time, against 8000 GB/s
+  cpu_baseline  the CPU oracle timed on sampled query rows, extrapolated by pair count
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(seqlens, w0, Hq, D):
+    pc = sum(L * (L + 1) // 2 for L in seqlens)
+    pw = 0
+    for L in seqlens:
+        m = min(L, w0)
+        pw += m * (m + 1) // 2 + (L - m) * w0
+    return 4 * D * Hq * pc + 2 * D * Hq * pw, 4 * D * Hq * pc
+
+
+def bench_prefill(bf, torch, W, steps, warmup):
+    w = W.get("qwen3_4b_128k")
+    T = w.total_tokens
+    q, k, v = W.raw_inputs_torch(w, "cuda")
+    # standard RoPE at absolute positions, built with the library's own rope_apply
+    bf.rope_apply(q, w.theta)
+    bf.rope_apply(k, w.theta)
+    cu = [int(c) for c in w.cu_seqlens]
+    out = torch.empty_like(q)
+    lse = torch.empty((w.Hq, T), dtype=torch.float32, device="cuda")
+    ws = bf.Workspace.for_op(bf.OP_PREFILL, max(w.seqlens), w.Hq, w.Hkv, w.D)
+    call = lambda: bf.bifocal_prefill(q, k, v, cu, w.w0, w.w_pretrained, w.theta, out=out,
+                                      lse=lse, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    F, Fc = prefill_flops(w.seqlens, w.w0, w.Hq, w.D)
+    assert bool(torch.isfinite(out).all())
+    return w, ms, F, Fc
+
+
+def bench_decode(bf, torch, W, passes, warmup):
+    w = W.get("qwen3_8b_decode_128k")
+    q, k, v = W.raw_inputs_torch(w, "cuda")
+    bf.rope_apply(k, w.theta)
+    positions = w.decode_positions()
+    pos_t = torch.as_tensor(positions.astype(np.int32), device="cuda")
+    bf.rope_apply(q, w.theta, pos=pos_t)  # query of step t at its own position
+    ws = bf.Workspace.for_op(bf.OP_DECODE, w.cache_len, w.Hq, w.Hkv, w.D)
+    o = torch.empty((w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.Hq,), dtype=torch.float32, device="cuda")
+
+    def one_pass():
+        for t, pos in enumerate(positions):
+            bf.bifocal_decode(q[t], k, v, int(pos), w.w0, w.w_pretrained, w.theta, out=o,
+                              lse=lse, workspace=ws)
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(passes):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (passes * len(positions))
+    kv_bytes = float(np.mean([2 * (p + 1) * w.Hkv * w.D * 2 for p in positions]))
+    return w, ms_step, kv_bytes
+
+
+def cpu_baseline(W, F, n_uniform=200):
+    """The oracle as it stands, on sampled query rows of the 128K workload (all 32
+    heads), extrapolated to the whole prefill by the number of causal pairs."""
+    from oracle.bifocal_ref import bifocal_rows, rope_rotate
+    w = W.get("qwen3_4b_128k")
+    L = w.total_tokens
+    q, k, v = W.raw_prefill_inputs(w)
+    rows = W.sample_rows(L, w.w0, n_uniform, seed=w.seed, tile=64)
+    pos = np.arange(L)
+    Qs = rope_rotate(q[rows], rows, w.theta).astype(np.float32)
+    Ks = np.empty_like(k)
+    for c0 in range(0, L, 16384):
+        Ks[c0:c0 + 16384] = rope_rotate(k[c0:c0 + 16384], pos[c0:c0 + 16384], w.theta)
+    Qs, Ks, V = W.round_to_bf16(Qs), W.round_to_bf16(Ks), W.round_to_bf16(v)
+    del q, k, v
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    bifocal_rows(Qs, Ks, V, rows, w.w0, w.w_pretrained, w.theta, q_given_rows=True)
+    t = time.perf_counter() - t0
+    pairs_sampled = float(np.sum(rows + 1))
+    pairs_total = L * (L + 1) / 2.0
+    t_full = t * pairs_total / pairs_sampled
+    return {"value": F / t_full / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(rows)} query rows x {w.Hq} heads of qwen3_4b_128k "
+                      f"({t:.1f} s), extrapolated by causal pair count to all "
+                      f"{L} rows (t_full = {t_full:.0f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-passes", type=int, default=2,
+                    help="timed passes of the 256-step decode workload")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dynamic_rope_context_amd as bf
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    bf.lib()
+
+    result = {}
+    if args.only in ("all", "prefill"):
+        log("prefill: qwen3_4b_128k")
+        w, ms, F, Fc = bench_prefill(bf, torch, W, args.steps, args.warmup)
+        tflops = F / (ms * 1e-3) / 1e12
+        log(f"prefill: {ms:.2f} ms/call, {tflops:.1f} TFLOP/s counted, "
+            f"{Fc / (ms * 1e-3) / 1e12:.1f} TFLOP/s causal-only")
+        result.update({
+            "metric": "bifocal prefill TFLOP/s (% bf16 MFMA peak) at 128K; decode KV GB/s",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded normal q/k/v with outlier channels; no weights)",
+            "config": {"workload": "qwen3_4b_128k", "batch": 1, "seq_len": w.total_tokens,
+                       "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D, "w0": w.w0,
+                       "w_pretrained": w.w_pretrained, "G": 4, "theta": w.theta},
+            "flops_per_step": F, "causal_flops_per_step": Fc,
+            "causal_tflops": round(Fc / (ms * 1e-3) / 1e12, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        })
+    if args.only in ("all", "decode"):
+        log("decode: qwen3_8b_decode_128k, 256 steps per pass")
+        w, ms_step, kv_bytes = bench_decode(bf, torch, W, args.decode_passes, 1)
+        gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+        log(f"decode: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s of K+V")
+        dec = {"workload": "qwen3_8b_decode_128k", "steps_per_pass": w.decode_steps,
+               "passes": args.decode_passes, "us_per_step": round(ms_step * 1e3, 2),
+               "kv_bytes_per_step": kv_bytes, "kv_GBps": round(gbs, 1),
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": None}}
+        if "metric" in result:
+            result["decode"] = dec
+        else:
+            result.update({"metric": "bifocal decode KV GB/s at 128K", "value": dec["kv_GBps"],
+                           "unit": "GB/s", "n_gpus": 1, "steps": args.decode_passes,
+                           "warmup": 1, "ms_per_step": round(ms_step * w.decode_steps, 4),
+                           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                           "dtype": "bf16", "data": "synthetic",
+                           "config": {"workload": "qwen3_8b_decode_128k"},
+                           "roofline": dec["roofline"]})
+    if args.only in ("all", "prefill") and not args.no_cpu_baseline:
+        log("cpu baseline: oracle on sampled rows")
+        result["cpu_baseline"] = cpu_baseline(W, result["flops_per_step"])
+        log(f"cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,91 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times: every output row is computed on the GPU, and sampled rows (first/last rows,
+rows around w0, tile and aliasing-group boundaries, uniform draws) of every head are
+compared with the CPU oracle, which computes each row from its definition."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle.bifocal_ref import bifocal_decode_ref, bifocal_rows, group_size
+from helpers import BF16_TOL, decode_inputs, errors, prefill_inputs, std_query, within
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def bf():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import dynamic_rope_context_amd as m
+    m.lib()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+
+
+def _prefill_case(bf, name, n_uniform):
+    w = W.get(name)
+    say(f"{name}: building inputs on the CPU")
+    Q, K, V, cu = prefill_inputs(w)
+    say(f"{name}: GPU prefill")
+    O, lse = bf.bifocal_prefill(dev(Q), dev(K), dev(V), [int(c) for c in cu], w.w0,
+                                w.w_pretrained, w.theta)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all())
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        L = e - s
+        G = group_size(L, w.w_pretrained)
+        rows = W.sample_rows(L, w.w0, n_uniform, seed=w.seed + b, tile=64,
+                             extra=(G * 1000 - 1, G * 1000, w.w0 + 63, w.w0 + 64))
+        Og = O[s + rows].float().cpu().numpy()
+        Lg = lse[:, s + rows].T.cpu().numpy()
+        say(f"{name}: oracle on {len(rows)} rows x {w.Hq} heads of sequence {b} (L={L}, G={G})")
+        Or, Lr = bifocal_rows(Q[s:e], K[s:e], V[s:e], rows, w.w0, w.w_pretrained, w.theta)
+        err = errors(Og, Or, Lg, Lr)
+        say(f"{name}: seq {b} {err}")
+        assert within(err, BF16_TOL), err
+
+
+def test_qwen3_1p7b_32k_g1(bf):
+    _prefill_case(bf, "qwen3_1p7b_32k_g1", 40)
+
+
+def test_qwen3_4b_128k(bf):
+    _prefill_case(bf, "qwen3_4b_128k", 24)
+
+
+def test_qwen3_8b_ragged(bf):
+    _prefill_case(bf, "qwen3_8b_ragged", 16)
+
+
+def test_qwen3_8b_decode_128k(bf):
+    w = W.get("qwen3_8b_decode_128k")
+    say("decode: building the cache on the CPU")
+    q_raw, Kc, Vc = decode_inputs(w)
+    Kd, Vd = dev(Kc), dev(Vc)
+    ws = bf.Workspace.for_op(bf.OP_DECODE, w.cache_len, w.Hq, w.Hkv, w.D)
+    positions = w.decode_positions()
+    checked = {0, 1, len(positions) // 2, len(positions) - 1}
+    for step, pos in enumerate(positions):
+        q = std_query(q_raw[step], int(pos), w.theta, "bf16")
+        o, lse = bf.bifocal_decode(dev(q), Kd, Vd, int(pos), w.w0, w.w_pretrained, w.theta,
+                                   workspace=ws)
+        if step in checked:
+            torch.cuda.synchronize()
+            Or, Lr = bifocal_decode_ref(q, Kc, Vc, int(pos), w.w0, w.w_pretrained, w.theta)
+            err = errors(o.float().cpu().numpy(), Or, lse.cpu().numpy(), Lr)
+            say(f"decode step {step} pos={int(pos)} G={group_size(int(pos) + 1, w.w_pretrained)}"
+                f" {err}")
+            assert within(err, BF16_TOL), err
+    torch.cuda.synchronize()

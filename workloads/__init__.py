@@ -180,3 +180,29 @@ def sample_rows(L: int, w0: int, n_uniform: int, seed: int, tile: int = 64,
     rng = _rng(seed)
     rows.update(int(r) for r in rng.integers(0, L, size=n_uniform))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Device-side draws for the benchmark (same distributions, torch's generator)
+# ---------------------------------------------------------------------------
+
+def raw_inputs_torch(w: Workload, device="cuda", T: Optional[int] = None, dtype=None):
+    """Raw q [T,Hq,D] (or [decode_steps,Hq,D] for decode), k, v [T,Hkv,D] drawn on the
+    device with torch.Generator(seed); outlier channels chosen as in the numpy path.
+    Values are rounded to ``dtype`` (default: the workload's dtype)."""
+    import torch
+    dt = dtype or (torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    T = (w.total_tokens if T is None else T)
+    nq = T if w.kind == "prefill" else max(1, w.decode_steps)
+    out = []
+    for off, shape, hkey in ((1, (nq, w.Hq, w.D), 4), (2, (T, w.Hkv, w.D), 5),
+                             (3, (T, w.Hkv, w.D), None)):
+        g = torch.Generator(device=device)
+        g.manual_seed(w.seed + off)
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if w.outliers and hkey is not None:
+            ch = outlier_channels(w.seed + hkey, shape[1], w.D, w.outliers)
+            for h in range(shape[1]):
+                x[:, h, torch.as_tensor(ch[h], device=device)] *= w.outlier_scale
+        out.append(x.to(dt))
+    return tuple(out)
