@@ -91,9 +91,26 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
+// One float -> fp16 bits, round to nearest even, through the scalar conversion.  Every
+// fp16 operand of the remote branch (main operands and the hi/lo split) goes through
+// this one function so that the split always completes the exact hi value the main
+// MFMA used; the packed two-value form, when the compiler chose it for some operands
+// only, broke that match.
+__device__ __forceinline__ uint32_t f16_bits_of(float a) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a);
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return f16_bits_of(a) | (f16_bits_of(b) << 16);
+}
+// 2^x with the hardware instruction (inputs far below -126 flush to 0, which is what a
+// softmax weight that small should be).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // theta_m = theta^(-2m/D) and the angle p * theta_m in float64.
 __device__ __forceinline__ double inv_freq64(double theta, int m, int D) {

@@ -254,29 +254,61 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 }
 
 // Merge the splits of each query head: O = sum_s w_s acc_s / sum_s w_s l_s with
-// w_s = 2^(m_s - max m); LSE = ln 2 * (max m + log2 sum_s w_s l_s).
-template <typename TOut, int D>
-__global__ void __launch_bounds__(D) decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* base = a.part + (size_t)h * a.nsplit * (D + 2);
-  float mx = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, base[(size_t)s * (D + 2) + D]);
-  float o = 0.f, l = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* p = base + (size_t)s * (D + 2);
-    const float ms = p[D];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - mx);
-    o += w * p[d];
-    l += w * p[D + 1];
+// w_s = 2^(m_s - max m); LSE = ln 2 * (max m + log2 sum_s w_s l_s).  One workgroup per
+// query head; the splits are spread over the threads (the partials are read once).
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, u) : v + u;
   }
-  const float val = o / l;
-  if constexpr (sizeof(TOut) == 2)
-    ((uint16_t*)a.o)[(size_t)h * D + d] = (uint16_t)f32_to_bf16_bits(val);
-  else
-    ((float*)a.o)[(size_t)h * D + d] = val;
-  if (a.lse && d == 0) a.lse[h] = (mx + log2f(l)) * 0.69314718055994530942f;
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  v = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+  return v;
+}
+
+template <typename TOut, int D>
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
+  __shared__ float s_w[kDecodeMaxSplits];
+  __shared__ float s_red[4];
+  __shared__ float s_o[256];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ns = a.nsplit;
+  const float* base = a.part + (size_t)h * ns * (D + 2);
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, base[(size_t)s * (D + 2) + D]);
+  mx = block_reduce(mx, true, s_red);
+  float lsum = 0.f;
+  for (int s = tid; s < ns; s += 256) {
+    const float ms = base[(size_t)s * (D + 2) + D];
+    const float w = ms == -INFINITY ? 0.f : exp2f(ms - mx);
+    s_w[s] = w;
+    lsum += w * base[(size_t)s * (D + 2) + D + 1];
+  }
+  lsum = block_reduce(lsum, false, s_red);  // its barriers also publish s_w
+  constexpr int GROUPS = 256 / D;
+  const int d = tid % D, grp = tid / D;
+  float o = 0.f;
+#pragma unroll 8
+  for (int s = grp; s < ns; s += GROUPS) o += s_w[s] * base[(size_t)s * (D + 2) + d];
+  s_o[tid] = o;
+  __syncthreads();
+  if (tid < D) {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < GROUPS; ++q) v += s_o[q * D + tid];
+    const float val = v / lsum;
+    if constexpr (sizeof(TOut) == 2)
+      ((uint16_t*)a.o)[(size_t)h * D + tid] = (uint16_t)f32_to_bf16_bits(val);
+    else
+      ((float*)a.o)[(size_t)h * D + tid] = val;
+    if (a.lse && tid == 0) a.lse[h] = (mx + log2f(lsum)) * 0.69314718055994530942f;
+  }
 }
 
 template <typename TIn, int D>
@@ -291,7 +323,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int rep, hipStream_t stre
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<TIn, D>), dim3(a.Hq), dim3(D), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<TIn, D>), dim3(a.Hq), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -38,11 +38,11 @@ namespace bifocal {
 
 namespace mf {
 constexpr int D = 128;
-constexpr int BK = 64;        // keys per tile
+constexpr int BK = 32;        // keys per tile (one 32-row MFMA block)
 constexpr int NW = 8;         // waves per workgroup (32 query rows each)
 constexpr int ROWS = 256;     // query rows (head, position) per workgroup
 constexpr int KS_LD = D + 8;  // LDS row stride (16-bit elements) of the K arrays: 272 B
-constexpr int VT_LD = BK + 4; // LDS row stride of transposed V: 136 B
+constexpr int VT_LD = BK + 8; // LDS row stride of transposed V: 80 B (conflict-free writes)
 constexpr int KC_LD = 16;     // LDS row of the hi/lo correction operand: 32 B
 constexpr float kLazy = 8.f;  // allowed growth of the running max before a rescale
 
@@ -52,31 +52,31 @@ struct Stage {
   uint16_t kc[BK * KC_LD];  // [lo of 8 selected channels | hi of them], fp16 bits
   uint16_t vt[D * VT_LD];   // V^T, bf16 bits
 };
-constexpr size_t kSmem = 2 * sizeof(Stage);
+constexpr int NSTAGE = 3;     // tile t computed while t+1 is scored and t+2 staged
+constexpr size_t kSmem = NSTAGE * sizeof(Stage);
 
 enum { kRemote = 0, kStraddle = 1, kLocal = 2 };
 }  // namespace mf
 
 // R(-n) with the table entry (cos, sin) of n: (x1, x2) -> (x1 c + x2 s, x2 c - x1 s).
-// Written with explicit roundings so that every caller gets identical bits.
+// Written with explicit roundings so that every caller gets identical bits.  The empty
+// asm pins the float32 results: without it the compiler may fold "fma, then convert to
+// fp16" into one mixed-precision FMA that rounds once, straight to fp16, at some call
+// sites and not at others, and the hi/lo split must see the very hi value the main
+// operand carries.
 __device__ __forceinline__ void rot_neg(float x1, float x2, float c, float s, float& y1,
                                         float& y2) {
   y1 = __fmaf_rn(x1, c, __fmul_rn(x2, s));
   y2 = __fmaf_rn(x2, c, -__fmul_rn(x1, s));
+  asm volatile("" : "+v"(y1), "+v"(y2));
 }
 
-__device__ __forceinline__ uint32_t f16_bits(_Float16 h) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-// fp16 hi part (round to nearest even) and the fp16 remainder.
+// fp16 hi part and the fp16 remainder, from the same conversion as the main remote
+// operands (pack_f16), so the correction completes exactly the hi value they carry.
 __device__ __forceinline__ void split_f16(float y, uint32_t& hi, uint32_t& lo) {
-  const _Float16 h = (_Float16)y;
-  const _Float16 l = (_Float16)(y - (float)h);
-  hi = f16_bits(h);
-  lo = f16_bits(l);
-}
-__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  return f16_bits((_Float16)a) | (f16_bits((_Float16)b) << 16);
+  hi = f16_bits_of(y);
+  const float hf = (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
+  lo = f16_bits_of(y - hf);
 }
 
 __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
@@ -258,78 +258,77 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   };
 
   // ---- K/V staging: global -> registers -> LDS --------------------------------------
-  // K: thread (key kr_ = tid/8, eighth kq = tid%8) holds channels 8kq..8kq+7 and their
-  //    RoPE partners 64+8kq..; V: thread (key pair vr = tid%32, chunk vc = tid/32) holds
-  //    channels 8vc..8vc+7 of keys 2vr, 2vr+1; the hi/lo correction of key tid/4, pair
-  //    tid%4 is done by the first 256 threads.
-  const int kr_ = tid >> 3, kq = tid & 7;
-  const int vr = tid & 31, vc = tid >> 5;
-  const int cr = (tid >> 2) & 63, cp = tid & 3;
+  // K: thread (key kr_ = tid/16, pair group kq = tid%16) holds channels 4kq..4kq+3 and
+  //    their RoPE partners 64+4kq..; V: thread (key pair vr = tid%16, chunk vc = tid/16)
+  //    holds channels 4vc..4vc+3 of keys 2vr, 2vr+1; the hi/lo correction of key tid/4,
+  //    pair tid%4 is done by the first 128 threads.
+  const int kr_ = tid >> 4, kq = tid & 15;
+  const int vr = tid & 15, vc = tid >> 4;
+  const int cr = (tid >> 2) & (BK - 1), cp = tid & 3;
   const bool c_thread = tid < 4 * BK;
   const int my_sel = args.sel[g * kSelPairs + cp];
-  uint4 kraw[2], vraw[2];
+  uint2 kraw[2], vraw[2];
   uint32_t ccor[2];   // selected pair (x1, x2) of key cr, pair my_sel, bf16 bits
+  float4 ktab[2];     // (cos, sin) of pairs 4kq .. 4kq+3 at n(key kr_) for the remote copy
+  float2 ctab;        // (cos, sin) of pair my_sel at n(key cr)
   auto stage_load = [&](int kt) __attribute__((always_inline)) {
     const int j0 = kt * BK;
+    const bool remote_copy = kt < ktB;  // remote or straddling tile: rotate its keys
     {
       const int j = min(j0 + kr_, L - 1);
-      const uint16_t* row = Kp + ((size_t)(start + j) * Hkv + g) * D + 8 * kq;
-      kraw[0] = *reinterpret_cast<const uint4*>(row);
-      kraw[1] = *reinterpret_cast<const uint4*>(row + 64);
+      const uint16_t* row = Kp + ((size_t)(start + j) * Hkv + g) * D + 4 * kq;
+      kraw[0] = *reinterpret_cast<const uint2*>(row);
+      kraw[1] = *reinterpret_cast<const uint2*>(row + 64);
+      if (remote_copy) {
+        const float4* trow =
+            reinterpret_cast<const float4*>(tab + (size_t)(j - alias_pos(j, G)) * 64 + 4 * kq);
+        ktab[0] = trow[0];
+        ktab[1] = trow[1];
+      }
     }
-    if (c_thread) {
+    if (c_thread && remote_copy) {
       const int j = min(j0 + cr, L - 1);
       const uint16_t* row = Kp + ((size_t)(start + j) * Hkv + g) * D;
       ccor[0] = row[my_sel];
       ccor[1] = row[my_sel + 64];
+      ctab = tab[(size_t)(j - alias_pos(j, G)) * 64 + my_sel];
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const int j = min(j0 + 2 * vr + k2, L - 1);
-      vraw[k2] = *reinterpret_cast<const uint4*>(Vp + ((size_t)(start + j) * Hkv + g) * D + 8 * vc);
+      vraw[k2] = *reinterpret_cast<const uint2*>(Vp + ((size_t)(start + j) * Hkv + g) * D + 4 * vc);
     }
   };
-  auto stage_store = [&](int kt, int mode, Stage& st) __attribute__((always_inline)) {
-    const int j0 = kt * BK;
+  auto stage_store = [&](int kt, Stage& st) __attribute__((always_inline)) {
+    const int mode = kt < ktA ? kRemote : kt < ktB ? kStraddle : kLocal;
     if (mode != kRemote) {
-      uint16_t* dst = st.ks + kr_ * KS_LD + 8 * kq;
-      *reinterpret_cast<uint4*>(dst) = kraw[0];
-      *reinterpret_cast<uint4*>(dst + 64) = kraw[1];
+      uint16_t* dst = st.ks + kr_ * KS_LD + 4 * kq;
+      *reinterpret_cast<uint2*>(dst) = kraw[0];
+      *reinterpret_cast<uint2*>(dst + 64) = kraw[1];
     }
     if (mode != kLocal) {
-      {
-        const int j = min(j0 + kr_, L - 1);
-        const int n = j - alias_pos(j, G);
-        const float4* trow = reinterpret_cast<const float4*>(tab + (size_t)n * 64 + 8 * kq);
-        float y1[8], y2[8];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float4 cs = trow[e2];  // pairs 8kq + 2e2, +1
-          rot_neg(bf16_at(kraw[0], 2 * e2), bf16_at(kraw[1], 2 * e2), cs.x, cs.y, y1[2 * e2],
-                  y2[2 * e2]);
-          rot_neg(bf16_at(kraw[0], 2 * e2 + 1), bf16_at(kraw[1], 2 * e2 + 1), cs.z, cs.w,
-                  y1[2 * e2 + 1], y2[2 * e2 + 1]);
-        }
-        uint16_t* dst = st.kr + kr_ * KS_LD + 8 * kq;
-        *reinterpret_cast<uint4*>(dst) =
-            make_uint4(pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
-                       pack_f16(y1[6], y1[7]));
-        *reinterpret_cast<uint4*>(dst + 64) =
-            make_uint4(pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]), pack_f16(y2[4], y2[5]),
-                       pack_f16(y2[6], y2[7]));
-      }
+      float y1[4], y2[4];
+      const float x1[4] = {bf16_lo(kraw[0].x), bf16_hi(kraw[0].x), bf16_lo(kraw[0].y),
+                           bf16_hi(kraw[0].y)};
+      const float x2[4] = {bf16_lo(kraw[1].x), bf16_hi(kraw[1].x), bf16_lo(kraw[1].y),
+                           bf16_hi(kraw[1].y)};
+      rot_neg(x1[0], x2[0], ktab[0].x, ktab[0].y, y1[0], y2[0]);
+      rot_neg(x1[1], x2[1], ktab[0].z, ktab[0].w, y1[1], y2[1]);
+      rot_neg(x1[2], x2[2], ktab[1].x, ktab[1].y, y1[2], y2[2]);
+      rot_neg(x1[3], x2[3], ktab[1].z, ktab[1].w, y1[3], y2[3]);
+      uint16_t* dst = st.kr + kr_ * KS_LD + 4 * kq;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]));
+      *reinterpret_cast<uint2*>(dst + 64) =
+          make_uint2(pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]));
       // hi/lo of the selected pair cp for key cr: [lo ch0..7 | hi ch0..7],
       // channel k = pair (k % 4), component (k / 4).
       if (c_thread) {
-        const int j = min(j0 + cr, L - 1);
-        const int n = j - alias_pos(j, G);
-        const float2 cs = tab[(size_t)n * 64 + my_sel];
-        float y1, y2;
-        rot_neg(__uint_as_float(ccor[0] << 16), __uint_as_float(ccor[1] << 16), cs.x, cs.y, y1,
-                y2);
+        float z1, z2;
+        rot_neg(__uint_as_float(ccor[0] << 16), __uint_as_float(ccor[1] << 16), ctab.x, ctab.y,
+                z1, z2);
         uint32_t h1, l1, h2, l2;
-        split_f16(y1, h1, l1);
-        split_f16(y2, h2, l2);
+        split_f16(z1, h1, l1);
+        split_f16(z2, h2, l2);
         uint16_t* row = st.kc + cr * KC_LD;
         row[cp] = (uint16_t)l1;
         row[4 + cp] = (uint16_t)l2;
@@ -338,17 +337,12 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       }
     }
     // V^T: vt[d][key], keys (2vr, 2vr+1) packed per 32-bit word
-    {
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vraw[0]);  // key 2vr, d 8vc..+7
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vraw[1]);  // key 2vr+1
-      uint32_t* dst = reinterpret_cast<uint32_t*>(st.vt) + vr;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d = 8 * vc + 2 * w;
-        dst[(d * VT_LD) / 2] = __byte_perm(a0[w], a1[w], 0x5410);
-        dst[((d + 1) * VT_LD) / 2] = __byte_perm(a0[w], a1[w], 0x7632);
-      }
-    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(st.vt) + vr;
+    const int d0 = 4 * vc;
+    dst[((d0 + 0) * VT_LD) / 2] = __byte_perm(vraw[0].x, vraw[1].x, 0x5410);
+    dst[((d0 + 1) * VT_LD) / 2] = __byte_perm(vraw[0].x, vraw[1].x, 0x7632);
+    dst[((d0 + 2) * VT_LD) / 2] = __byte_perm(vraw[0].y, vraw[1].y, 0x5410);
+    dst[((d0 + 3) * VT_LD) / 2] = __byte_perm(vraw[0].y, vraw[1].y, 0x7632);
   };
 
   // ---- softmax state and output accumulators --------------------------------------
@@ -356,129 +350,111 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   float m_run = -1e30f, l_run = 0.f;
   const float c2 = args.scale * 1.4426950408889634f;  // scale * log2(e)
 
-  auto tile_mode = [&](int kt) { return kt < ktA ? kRemote : kt < ktB ? kStraddle : kLocal; };
-
-  // One tile of BK keys in two 32-key halves (mb): scores, online softmax, PV.
-  auto compute = [&](int kt, const Stage& st, auto mode_c, bool need_mask)
-      __attribute__((always_inline)) {
-    constexpr int mode = decltype(mode_c)::value;
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    if constexpr (mode == kLocal) {
+  // Scores S^T (32 keys x this wave's 32 queries) of tile kt, by tile class.
+  auto qk = [&](int kt, const Stage& st) __attribute__((always_inline)) -> f32x16 {
+    f32x16 sacc = f32x16{};
+    const uint16_t* krow_s = st.ks + ln * KS_LD + 8 * hf;
+    const uint16_t* krow_r = st.kr + ln * KS_LD + 8 * hf;
+    if (kt >= ktB) {  // local
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(st.ks + (32 * mb + ln) * KS_LD + 16 * s + 8 * hf);
-          sacc[mb] = mfma_bf16(a, qop[s], sacc[mb]);
-        }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(st.kr + (32 * mb + ln) * KS_LD + 16 * s + 8 * hf);
-          sacc[mb] = mfma_f16(a, qop[s], sacc[mb]);
-        }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(st.kc + (32 * mb + ln) * KC_LD + 8 * hf);
-        sacc[mb] = mfma_f16(a, qcor, sacc[mb]);
-      }
+        sacc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow_s + 16 * s), qop[s], sacc);
+      return sacc;
     }
-    if constexpr (mode == kStraddle) {
-      // local scores with the exact bf16 operands, selected per pair by distance
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      sacc = mfma_f16(*reinterpret_cast<const u32x4*>(krow_r + 16 * s), qop[s], sacc);
+    sacc = mfma_f16(*reinterpret_cast<const u32x4*>(st.kc + ln * KC_LD + 8 * hf), qcor, sacc);
+    if (kt >= ktA) {  // straddle: standard scores inside the window, selected per pair
       u32x4 qs[8];
       load_q_std(qs);
+      f32x16 sl = f32x16{};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 sl = f32x16{};
+      for (int s = 0; s < 8; ++s)
+        sl = mfma_bf16(*reinterpret_cast<const u32x4*>(krow_s + 16 * s), qs[s], sl);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(st.ks + (32 * mb + ln) * KS_LD + 16 * s + 8 * hf);
-          sl = mfma_bf16(a, qs[s], sl);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kt * BK + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (qi - j < w0) sacc[mb][r] = sl[r];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int j = kt * BK + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (qi - j < w0) sacc[r] = sl[r];
       }
     }
+    return sacc;
+  };
 
-    // ---- online softmax (per query column, both lane halves) ----
-    if (need_mask) {
+  // Online softmax of one tile's scores (in place -> probabilities) and O^T += V^T P^T.
+  auto softmax_pv = [&](int kt, f32x16 sacc, const Stage& st) __attribute__((always_inline)) {
+    if (kt * BK + BK - 1 > i0) {  // causal diagonal or ragged tail inside this tile
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kt * BK + 32 * mb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (j > qi || j >= L) sacc[mb][r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int j = kt * BK + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (j > qi || j >= L) sacc[r] = -INFINITY;
+      }
     }
-    float mx = -INFINITY;
+    float mx = sacc[0];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float cand = fmaxf(m_run, mx * c2);
     const bool need = cand > m_run + kLazy;
     if (__ballot(need)) {
       const float m_new = need ? cand : m_run;
-      const float f = exp2f(m_run - m_new);
+      const float f = fast_exp2(m_run - m_new);
       l_run *= f;
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= f;
       m_run = m_new;
     }
     const float mneg = -m_run;
+    uint32_t pk[8];
     float lsum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(__fmaf_rn(sacc[mb][r], c2, mneg));
-        sacc[mb][r] = p;
-        lsum += p;
-      }
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(__fmaf_rn(sacc[r], c2, mneg));
+      const float p1 = fast_exp2(__fmaf_rn(sacc[r + 1], c2, mneg));
+      lsum += p0 + p1;
+      pk[r / 2] = pack_bf16(p0, p1);
+    }
     l_run += lsum;
-
-    // ---- O^T += V^T P^T (four K=16 steps) ----
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pb = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+      const int kofs = 16 * t + 4 * hf;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const f32x16& sv = sacc[mb];
-        const u32x4 pb = u32x4{pack_bf16(sv[8 * t + 0], sv[8 * t + 1]), pack_bf16(sv[8 * t + 2], sv[8 * t + 3]),
-                               pack_bf16(sv[8 * t + 4], sv[8 * t + 5]), pack_bf16(sv[8 * t + 6], sv[8 * t + 7])};
-        const int kofs = 32 * mb + 16 * t + 4 * hf;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint16_t* vrow = st.vt + (32 * db + ln) * VT_LD + kofs;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          oacc[db] = mfma_bf16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, oacc[db]);
-        }
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* vrow = st.vt + (32 * db + ln) * VT_LD + kofs;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        oacc[db] = mfma_bf16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, oacc[db]);
       }
+    }
   };
 
-  // ---- main loop: remote tiles, then straddling tiles, then local tiles ----------
-  auto iteration = [&](int kt, auto mode_c) __attribute__((always_inline)) {
-    constexpr int mode = decltype(mode_c)::value;
-    __syncthreads();
-    if (kt + 1 < nkt) stage_load(kt + 1);
-    const bool need_mask = mode != kRemote && kt * BK + BK - 1 > i0;  // diagonal / tail
-    compute(kt, stg[kt & 1], mode_c, need_mask);
-    if (kt + 1 < nkt) stage_store(kt + 1, tile_mode(kt + 1), stg[(kt + 1) & 1]);
-  };
+  // ---- software-pipelined main loop ----------------------------------------------
+  // Iteration t: stage loads of tile t+2 are in flight, tile t+1 is scored (MFMA) while
+  // tile t goes through the softmax (VALU) and PV (MFMA), then tile t+2 is written to
+  // LDS.  Three LDS stages; one barrier per tile.
   if (ktB > 0) load_q_remote();
+  else load_q_std(qop);
   stage_load(0);
-  stage_store(0, tile_mode(0), stg[0]);
-  int kt = 0;
-  for (; kt < ktA; ++kt) iteration(kt, std::integral_constant<int, kRemote>());
-  for (; kt < ktB; ++kt) iteration(kt, std::integral_constant<int, kStraddle>());
-  load_q_std(qop);
-  for (; kt < nkt; ++kt) iteration(kt, std::integral_constant<int, kLocal>());
+  stage_store(0, stg[0]);
+  if (nkt > 1) {
+    stage_load(1);
+    stage_store(1, stg[1]);
+  }
+  __syncthreads();
+  f32x16 s_cur = qk(0, stg[0]);
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 2 < nkt) stage_load(kt + 2);
+    f32x16 s_next = f32x16{};
+    if (kt + 1 < nkt) {
+      if (kt + 1 == ktB && ktB > 0) load_q_std(qop);  // scores switch to local tiles
+      s_next = qk(kt + 1, stg[(kt + 1) % NSTAGE]);
+    }
+    softmax_pv(kt, s_cur, stg[kt % NSTAGE]);
+    if (kt + 2 < nkt) stage_store(kt + 2, stg[(kt + 2) % NSTAGE]);
+    __syncthreads();
+    s_cur = s_next;
+  }
 
   // ---- epilogue: O = O^T / l, LSE ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
