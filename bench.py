@@ -13,10 +13,15 @@ Prints one JSON line on stdout; progress goes to stderr.
   roofline   the prefill kernel against the dense bf16 MFMA peak (2500 TFLOP/s)
   decode     KV GB/s = bytes of K and V read per step / step time, against 8000 GB/s
   cpu_baseline  the CPU oracle timed on sampled query rows, extrapolated by pair count
+  traffic    HBM bytes per launch of the timed kernel from rocprofv3 FETCH_SIZE and
+             WRITE_SIZE counters (profiles/hbm_traffic.json), scaled by what the same
+             counters read for a plain 1 GiB device copy (``--only copy``); null when
+             the kernel source changed after the counters were taken.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +38,53 @@ PEAK_HBM_GBS = 8000.0
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+KERNEL_SOURCES = {
+    "prefill": ["dynamic_rope_context_amd/csrc/prefill_mfma.hip",
+                "dynamic_rope_context_amd/csrc/prefill_args.h",
+                "dynamic_rope_context_amd/csrc/bf_common.h"],
+    "decode": ["dynamic_rope_context_amd/csrc/decode.hip",
+               "dynamic_rope_context_amd/csrc/decode_args.h",
+               "dynamic_rope_context_amd/csrc/bf_common.h"],
+}
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def hbm_traffic(kind):
+    """Bytes moved to/from HBM per launch of the timed kernel, from the committed
+    counter summary; None if absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        k = rec[kind]
+        if k["source_sha256"] != source_hash(kind):
+            return None
+        c = rec["copy"]
+        f_fac = c["bytes_read"] / (c["FETCH_SIZE_KiB"] * 1024.0)
+        w_fac = c["bytes_written"] / (c["WRITE_SIZE_KiB"] * 1024.0)
+        return (k["FETCH_SIZE_KiB"] * f_fac + k["WRITE_SIZE_KiB"] * w_fac) * 1024.0
+    except (OSError, KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def bench_copy(torch, mib, reps):
+    """A plain device copy of known size: the calibration run for the HBM byte counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": reps}
 
 
 def prefill_flops(seqlens, w0, Hq, D):
@@ -147,7 +199,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-passes", type=int, default=2,
                     help="timed passes of the 256-step decode workload")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--decode-warmup", type=int, default=1)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="--only copy: bytes copied per launch, MiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -162,6 +217,9 @@ def main():
     bf.lib()
 
     result = {}
+    if args.only == "copy":
+        print(json.dumps(bench_copy(torch, args.copy_mib, args.steps)), flush=True)
+        return
     if args.only in ("all", "prefill"):
         log("prefill: qwen3_4b_128k")
         w, ms, F, Fc = bench_prefill(bf, torch, W, args.steps, args.warmup)
@@ -181,11 +239,13 @@ def main():
             "causal_tflops": round(Fc / (ms * 1e-3) / 1e12, 3),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": hbm_traffic("prefill")},
         })
     if args.only in ("all", "decode"):
         log("decode: qwen3_8b_decode_128k, 256 steps per pass")
-        w, ms_step, kv_bytes = bench_decode(bf, torch, W, args.decode_passes, 1)
+        w, ms_step, kv_bytes = bench_decode(bf, torch, W, args.decode_passes,
+                                            args.decode_warmup)
         gbs = kv_bytes / (ms_step * 1e-3) / 1e9
         log(f"decode: {ms_step * 1e3:.1f} us/step, {gbs:.0f} GB/s of K+V")
         dec = {"workload": "qwen3_8b_decode_128k", "steps_per_pass": w.decode_steps,
@@ -193,7 +253,7 @@ def main():
                "kv_bytes_per_step": kv_bytes, "kv_GBps": round(gbs, 1),
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "traffic": None}}
+                            "traffic": hbm_traffic("decode")}}
         if "metric" in result:
             result["decode"] = dec
         else:

@@ -147,6 +147,10 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
   }
   const int32_t T = cu_seqlens[B];
   if (D != 64 && D != 128) return BF_EUNSUPPORTED;
+  // positions must stay within the division-free alias range, and one sequence's rows
+  // within 32-bit element offsets
+  if (max_len >= kMaxPositions || (int64_t)max_len * std::max(Hq, Hkv) * D >= (1ll << 31))
+    return BF_EUNSUPPORTED;
   const int rep = Hq / Hkv;
   if (dt == BF_BF16 && (D != 128 || (rep != 1 && rep != 2 && rep != 4 && rep != 8)))
     return BF_EUNSUPPORTED;
@@ -195,6 +199,9 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
       a.seq[n].start = cu_seqlens[b];
       a.seq[n].len = L;
       a.seq[n].G = group_size(L, w_pretrained);
+      const DivMagic dm = div_magic((uint32_t)a.seq[n].G);
+      a.seq[n].gmul = dm.mul;
+      a.seq[n].gshift = dm.shift;
       maxq = std::max(maxq, (L + rows - 1) / rows);
       ++n;
     }
@@ -225,6 +232,7 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
   if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
   const WsLayout lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes);
   const int32_t n_keys = pos + 1;
+  if (n_keys >= kMaxPositions) return BF_EUNSUPPORTED;
   if (lay.scratch_off == 0 || lay.n_cap < n_keys) return BF_EWORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
@@ -255,6 +263,7 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
   a.Hkv = Hkv;
   a.w0 = w0;
   a.G = group_size((int64_t)pos + 1, w_pretrained);
+  a.gdiv = div_magic((uint32_t)a.G);
   a.nsplit = nsplit;
   a.kps = kps;
   const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt((double)D);

@@ -120,4 +120,23 @@ __device__ __forceinline__ double inv_freq64(double theta, int m, int D) {
 // f(x) = floor(x / G) and n(x) = x - f(x) for x >= 0.
 __device__ __forceinline__ int alias_pos(int x, int G) { return x / G; }
 
+// Division by G without a divide: for 0 <= x < 2^24, floor(x / G) =
+// (x * M) >> S with S = 24 + ceil(log2 G) and M = ceil(2^S / G).  (x*M/2^S exceeds
+// x/G by less than 2^24 / 2^S <= 1/G, which cannot reach the next integer.)
+struct DivMagic {
+  uint32_t mul;
+  uint32_t shift;
+};
+inline DivMagic div_magic(uint32_t G) {
+  uint32_t l = 0;
+  while ((1u << l) < G) ++l;
+  const uint32_t S = 24 + l;
+  const uint64_t M = ((1ull << S) + G - 1) / G;
+  return DivMagic{(uint32_t)M, S};
+}
+__device__ __forceinline__ int alias_fast(int x, DivMagic m) {
+  return (int)(((uint64_t)(uint32_t)x * m.mul) >> m.shift);
+}
+constexpr int kMaxPositions = 1 << 24;  // positions the magic division covers
+
 }  // namespace bifocal

@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   // Query rows of this KV head: standard copy and remote copy R(f(pos) - pos) q.
   float qs[REP][CPL], qr[REP][CPL];
   {
-    const int nq = pos - alias_pos(pos, G);
+    const int nq = pos - alias_fast(pos, a.gdiv);
     const TIn* qp = (const TIn*)a.q;
 #pragma unroll
     for (int h = 0; h < REP; ++h) {
@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       Row<TIn>::template load<CPL>(kr, kv[u]);
       Row<TIn>::template load<CPL>(vr, vv[u]);
       if constexpr (mode != kLocal) {
-        const int n = jc - alias_pos(jc, G);
+        const int n = jc - alias_fast(jc, a.gdiv);
         const float4* tp = reinterpret_cast<const float4*>(tab + (size_t)n * H2 + m0);
 #pragma unroll
         for (int c = 0; c < CPL; c += 2) {

@@ -14,6 +14,7 @@ struct DecodeArgs {
   void* o;             // [Hq, D]
   float* lse;          // [Hq] or null
   int32_t pos, Hq, Hkv, w0, G, nsplit, kps;  // kps: keys per split (multiple of 64)
+  DivMagic gdiv;                             // floor(x / G) without a divide
   float scale_log2;                          // softmax scale * log2(e)
 };
 

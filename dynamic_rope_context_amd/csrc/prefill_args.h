@@ -5,13 +5,15 @@
 
 namespace bifocal {
 
-constexpr int kMaxSeqPerLaunch = 64;
+constexpr int kMaxSeqPerLaunch = 48;
 
 struct SeqInfo {
   int32_t start;  // first token of the sequence in the packed [T, H, D] tensors
   int32_t len;    // L_b
   int32_t G;      // max(1, ceil(L_b / w_pretrained))
-  int32_t pad;
+  uint32_t gmul;  // floor(x / G) = (x * gmul) >> gshift for 0 <= x < 2^24
+  uint32_t gshift;
+  int32_t pad[3];
 };
 
 struct PrefillArgs {

@@ -182,6 +182,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   if (i0 >= L) return;
   const int start = args.seq[b].start;
   const int G = args.seq[b].G;
+  const DivMagic gdiv{args.seq[b].gmul, args.seq[b].gshift};
   const int Hq = args.Hq;
   const int i_end = min(L, i0 + BMPOS);  // exclusive
   // G = 1: the aliased positions are the true ones, every pair is "local".
@@ -220,7 +221,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       dst[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
   };
   auto load_q_remote = [&]() __attribute__((always_inline)) {
-    const int n = qrow_i - alias_pos(qrow_i, G);
+    const int n = qrow_i - alias_fast(qrow_i, gdiv);
     uint4 raw[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) raw[s] = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hf);
@@ -281,7 +282,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       kraw[1] = *reinterpret_cast<const uint2*>(row + 64);
       if (remote_copy) {
         const float4* trow =
-            reinterpret_cast<const float4*>(tab + (size_t)(j - alias_pos(j, G)) * 64 + 4 * kq);
+            reinterpret_cast<const float4*>(tab + (size_t)(j - alias_fast(j, gdiv)) * 64 + 4 * kq);
         ktab[0] = trow[0];
         ktab[1] = trow[1];
       }
@@ -291,7 +292,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       const uint16_t* row = Kp + ((size_t)(start + j) * Hkv + g) * D;
       ccor[0] = row[my_sel];
       ccor[1] = row[my_sel + 64];
-      ctab = tab[(size_t)(j - alias_pos(j, G)) * 64 + my_sel];
+      ctab = tab[(size_t)(j - alias_fast(j, gdiv)) * 64 + my_sel];
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
