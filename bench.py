@@ -106,7 +106,8 @@ def bench_prefill(bf, torch, W, steps, warmup):
     cu = [int(c) for c in w.cu_seqlens]
     out = torch.empty_like(q)
     lse = torch.empty((w.Hq, T), dtype=torch.float32, device="cuda")
-    ws = bf.Workspace.for_op(bf.OP_PREFILL, max(w.seqlens), w.Hq, w.Hkv, w.D)
+    ws = bf.Workspace.for_op(bf.OP_PREFILL, max(w.seqlens), w.Hq, w.Hkv, w.D,
+                             total_tokens=T, num_seqs=len(w.seqlens))
     call = lambda: bf.bifocal_prefill(q, k, v, cu, w.w0, w.w_pretrained, w.theta, out=out,
                                       lse=lse, workspace=ws)
     for _ in range(warmup):

@@ -45,7 +45,7 @@ def _load():
     lib.bifocal_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f32,
                                    i32, vp, sz, vp]
     lib.bifocal_decode.restype = i32
-    lib.bifocal_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.bifocal_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32]
     lib.bifocal_workspace_bytes.restype = sz
     lib.bifocal_status_string.argtypes = [i32]
     lib.bifocal_status_string.restype = ctypes.c_char_p
@@ -97,8 +97,12 @@ def group_size(L: int, w_pretrained: int) -> int:
     return int(lib().bifocal_group_size(int(L), int(w_pretrained)))
 
 
-def workspace_bytes(op: int, max_len: int, Hq: int, Hkv: int, D: int) -> int:
-    return int(lib().bifocal_workspace_bytes(op, max_len, Hq, Hkv, D))
+def workspace_bytes(op: int, max_len: int, Hq: int, Hkv: int, D: int,
+                    total_tokens: Optional[int] = None, num_seqs: int = 1) -> int:
+    """Workspace bytes for an operation; prefill also needs the largest token count and
+    batch size of the calls (defaults: one sequence of max_len tokens)."""
+    total = max_len if total_tokens is None else total_tokens
+    return int(lib().bifocal_workspace_bytes(op, max_len, total, num_seqs, Hq, Hkv, D))
 
 
 class Workspace:
@@ -113,8 +117,9 @@ class Workspace:
         self.nbytes = int(nbytes)
 
     @classmethod
-    def for_op(cls, op: int, max_len: int, Hq: int, Hkv: int, D: int, device="cuda"):
-        n = workspace_bytes(op, max_len, Hq, Hkv, D)
+    def for_op(cls, op: int, max_len: int, Hq: int, Hkv: int, D: int, device="cuda",
+               total_tokens: Optional[int] = None, num_seqs: int = 1):
+        n = workspace_bytes(op, max_len, Hq, Hkv, D, total_tokens, num_seqs)
         if n == 0:
             raise BifocalError("invalid workspace request")
         return cls(n, device)
@@ -159,7 +164,8 @@ def bifocal_prefill(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
         lse = torch.empty((Hq, T), dtype=torch.float32, device=Q.device)
     if workspace is None:
         max_len = max([cu[b + 1] - cu[b] for b in range(B)] + [0])
-        workspace = Workspace.for_op(OP_PREFILL, max(max_len, 1), Hq, Hkv, D, Q.device)
+        workspace = Workspace.for_op(OP_PREFILL, max(max_len, 1), Hq, Hkv, D, Q.device,
+                                     total_tokens=max(T, max_len, 1), num_seqs=max(B, 1))
     _check(lib().bifocal_prefill(
         _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
         _dev(lse, "lse") if lse is not None else 0,

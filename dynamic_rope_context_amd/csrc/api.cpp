@@ -25,7 +25,7 @@ hipError_t launch_table_ensure(void* ws, const WsLayout& lay, int D, double thet
 hipError_t launch_rope_apply(void* x, const int32_t* pos, int pos0, int T_, int H, int D,
                              double theta, int G, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& args, hipStream_t stream);
-hipError_t launch_prefill_mfma(const PrefillArgs& args, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillArgs& args, int chunk_tiles, hipStream_t stream);
 hipError_t launch_pair_select(const void* Q, const void* K, int T, int Hq, int Hkv,
                               uint32_t* mx, int32_t* sel, hipStream_t stream);
 int prefill_f32_rows_per_block();
@@ -108,11 +108,15 @@ const char* bifocal_status_string(int32_t s) {
 
 int32_t bifocal_group_size(int64_t L, int32_t w_pretrained) { return group_size(L, w_pretrained); }
 
-size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int32_t Hq, int32_t Hkv, int32_t D) {
+size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int64_t total_tokens,
+                               int32_t num_seqs, int32_t Hq, int32_t Hkv, int32_t D) {
   if (op < 0 || op > 2 || max_len < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || (D != 64 && D != 128))
     return 0;
   if (op == BF_OP_ROPE) return 0;
-  return ws_bytes_for(op, max_len, Hq, Hkv, D);
+  if (op == BF_OP_PREFILL && (total_tokens < max_len || num_seqs < 1 ||
+                              total_tokens > (int64_t)num_seqs * max_len))
+    return 0;
+  return ws_bytes_for(op, max_len, total_tokens, num_seqs, Hq, Hkv, D);
 }
 
 bf_status rope_apply(void* x, const int32_t* pos, int32_t pos0, int32_t T, int32_t H, int32_t D,
@@ -160,7 +164,14 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
       (lse && !aligned(lse, 4)))
     return BF_EINVAL;
   if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
-  const WsLayout lay = ws_layout(BF_OP_PREFILL, Hq, Hkv, D, ws_bytes);
+  // key-tile records (bf16 path): one per KV head and 32-key tile of every sequence
+  int64_t tiles = 0;
+  if (dt == BF_BF16)
+    for (int b = 0; b < B; ++b)
+      tiles += (cu_seqlens[b + 1] - cu_seqlens[b] + kKeyTileKeys - 1) / kKeyTileKeys;
+  if (tiles > INT32_MAX) return BF_EUNSUPPORTED;
+  const WsLayout lay =
+      ws_layout(BF_OP_PREFILL, Hq, Hkv, D, ws_bytes, dt == BF_BF16 ? records_bytes(Hkv, tiles) : 0);
   if (lay.scratch_off == 0 || lay.n_cap < max_len) return BF_EWORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
@@ -183,6 +194,8 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
   a.lse = lse;
   a.tab = reinterpret_cast<const float2*>(wsb + lay.table_off);
   a.sel = sel;
+  a.rec = reinterpret_cast<uint8_t*>(wsb + lay.rec_off);
+  a.tiles_total = (int32_t)tiles;
   a.T = T;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -191,11 +204,16 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
   a.scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
   const int rows = dt == BF_BF16 ? prefill_mfma_positions_per_block(rep)
                                  : prefill_f32_rows_per_block();
+  int32_t tile_base = 0;
   for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
-    int n = 0, maxq = 0;
+    int n = 0, maxq = 0, chunk_tiles = 0;
     for (int b = b0; b < std::min(B, b0 + kMaxSeqPerLaunch); ++b) {
       const int L = cu_seqlens[b + 1] - cu_seqlens[b];
       if (L == 0) continue;
+      const int nt = (L + kKeyTileKeys - 1) / kKeyTileKeys;
+      a.seq[n].tile_base = tile_base;
+      tile_base += nt;
+      chunk_tiles += nt;
       a.seq[n].start = cu_seqlens[b];
       a.seq[n].len = L;
       a.seq[n].G = group_size(L, w_pretrained);
@@ -208,7 +226,8 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
     if (n == 0) continue;
     a.nseq = n;
     a.max_qblocks = maxq;
-    hipError_t e = dt == BF_BF16 ? launch_prefill_mfma(a, st) : launch_prefill_f32(a, st);
+    hipError_t e = dt == BF_BF16 ? launch_prefill_mfma(a, chunk_tiles, st)
+                                 : launch_prefill_f32(a, st);
     if (e != hipSuccess) return BF_EHIP;
   }
   return BF_OK;
@@ -230,7 +249,7 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
       !aligned(o, dt == BF_BF16 ? 2 : 4) || (lse && !aligned(lse, 4)))
     return BF_EINVAL;
   if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
-  const WsLayout lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes);
+  const WsLayout lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes, 0);
   const int32_t n_keys = pos + 1;
   if (n_keys >= kMaxPositions) return BF_EUNSUPPORTED;
   if (lay.scratch_off == 0 || lay.n_cap < n_keys) return BF_EWORKSPACE;

@@ -37,16 +37,19 @@ static_assert(sizeof(TableHeader) == 256, "header is one 256-byte slot");
 
 constexpr uint64_t kTableMagic = 0x42464f43414c5442ull;  // "BTLACOFB"
 
-// Workspace layout: [header 256 B][table rows 0 .. n_cap-1][op scratch at the end].
+// Workspace layout: [header 256 B][table rows 0 .. n_cap-1][per-call records][op scratch].
 // The table offset does not depend on the operation, so prefill and decode calls can
-// share one workspace and its table.
+// share one workspace and its table; the records (prefill key tiles) and the op scratch
+// are carved from the end, and the table takes the room that is left.
 struct WsLayout {
-  size_t table_off, scratch_off, scratch_bytes;
+  size_t table_off, rec_off, scratch_off, scratch_bytes;
   int32_t n_cap;  // positions the table region can hold
 };
 
 constexpr int kDecodeMaxSplits = 512;
 constexpr int kSelPairs = 4;  // RoPE pairs per KV head given the hi/lo correction
+constexpr size_t kKeyTileBytes = 17408;  // one prefill key-tile record (32 keys, D = 128)
+constexpr int kKeyTileKeys = 32;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline size_t table_row_bytes(int D) { return (size_t)(D / 2) * 2 * sizeof(float); }
@@ -61,20 +64,33 @@ inline size_t scratch_bytes(int op, int Hq, int Hkv, int D) {
   return 0;
 }
 
-inline WsLayout ws_layout(int op, int Hq, int Hkv, int D, size_t ws_bytes) {
+// Key-tile records of a prefill call with `tiles` tiles per KV head.
+inline size_t records_bytes(int Hkv, int64_t tiles) {
+  return align_up((size_t)Hkv * (size_t)tiles * kKeyTileBytes, 256);
+}
+// Upper bound of the tiles of any batch of `num_seqs` sequences and `total` tokens.
+inline int64_t max_tiles(int64_t total, int64_t num_seqs) {
+  return (total + kKeyTileKeys - 1) / kKeyTileKeys + num_seqs;
+}
+
+inline WsLayout ws_layout(int op, int Hq, int Hkv, int D, size_t ws_bytes, size_t rec_bytes) {
   WsLayout l;
   l.table_off = 256;
   l.scratch_bytes = scratch_bytes(op, Hq, Hkv, D);
   const size_t ws = ws_bytes / 256 * 256;
-  l.scratch_off = ws > l.scratch_bytes ? ws - l.scratch_bytes : 0;
-  const size_t room = l.scratch_off > l.table_off ? l.scratch_off - l.table_off : 0;
+  const size_t tail = l.scratch_bytes + rec_bytes;
+  l.scratch_off = ws > tail ? ws - l.scratch_bytes : 0;
+  l.rec_off = ws > tail ? ws - tail : 0;
+  const size_t room = l.rec_off > l.table_off ? l.rec_off - l.table_off : 0;
   const size_t n = room / table_row_bytes(D);
   l.n_cap = n > (size_t)INT32_MAX ? INT32_MAX : (int32_t)n;
   return l;
 }
 
-inline size_t ws_bytes_for(int op, int max_len, int Hq, int Hkv, int D) {
-  return 256 + align_up((size_t)max_len * table_row_bytes(D), 256) +
+inline size_t ws_bytes_for(int op, int max_len, int64_t total, int64_t num_seqs, int Hq, int Hkv,
+                           int D) {
+  const size_t rec = op == 1 ? records_bytes(Hkv, max_tiles(total, num_seqs)) : 0;
+  return 256 + align_up((size_t)max_len * table_row_bytes(D), 256) + rec +
          scratch_bytes(op, Hq, Hkv, D);
 }
 

@@ -7,13 +7,26 @@ namespace bifocal {
 
 constexpr int kMaxSeqPerLaunch = 48;
 
+// Key-tile records written once per call by the key preparation pass and copied
+// verbatim into LDS by the bf16 prefill kernel.  One record per (KV head, tile of
+// kRecKeys keys of one sequence):
+//   kr  [kRecKeys][128]  fp16  R(f(j) - j) K_j                 8192 B
+//   kc  [kRecKeys][16]   fp16  hi/lo of the selected pairs     1024 B
+//   vt  [128][kRecKeys]  bf16  V^T                             8192 B
+// Keys past the end of the sequence are zero.
+constexpr int kRecKeys = 32;
+constexpr size_t kRecKr = 8192, kRecKc = 1024, kRecVt = 8192;
+constexpr size_t kRecBytes = kRecKr + kRecKc + kRecVt;
+static_assert(kRecBytes == kKeyTileBytes && kRecKeys == kKeyTileKeys, "workspace sizing");
+
 struct SeqInfo {
   int32_t start;  // first token of the sequence in the packed [T, H, D] tensors
   int32_t len;    // L_b
   int32_t G;      // max(1, ceil(L_b / w_pretrained))
   uint32_t gmul;  // floor(x / G) = (x * gmul) >> gshift for 0 <= x < 2^24
   uint32_t gshift;
-  int32_t pad[3];
+  int32_t tile_base;  // index of the sequence's first key-tile record
+  int32_t pad[2];
 };
 
 struct PrefillArgs {
@@ -24,7 +37,8 @@ struct PrefillArgs {
   float* lse;          // [Hq, T] or null
   const float2* tab;   // position table (cos, sin) [n][D/2]
   const int32_t* sel;  // [Hkv][kSelPairs] RoPE pairs given the hi/lo correction
-  int32_t T, Hq, Hkv, D, w0, nseq, max_qblocks, pad0;
+  uint8_t* rec;        // key-tile records [Hkv][tiles_total] (bf16 path)
+  int32_t T, Hq, Hkv, D, w0, nseq, max_qblocks, tiles_total;
   float scale;         // softmax scale (natural-log domain)
   float pad1;
   SeqInfo seq[kMaxSeqPerLaunch];

@@ -152,6 +152,106 @@ __global__ void pair_select_kernel(const uint32_t* __restrict__ mxq,
 }
 
 // ---------------------------------------------------------------------------
+// Key preparation: once per call, each key tile of each KV head is turned into the
+// record the main kernel copies into LDS verbatim (layout in prefill_args.h): the
+// remote copy R(f(j) - j) K_j rounded to fp16, the hi/lo correction of the selected
+// pairs, and V^T.  A key is rotated once here instead of once per query block that
+// reads it.  One workgroup (256 threads) per (tile, KV head).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
+  using namespace mf;
+  __shared__ __align__(16) uint16_t sv[BK][D + 8];
+  const int g = blockIdx.y;
+  const int t_local = blockIdx.x;
+  const int base0 = args.seq[0].tile_base;
+  int b = 0;
+  for (int q = 1; q < args.nseq; ++q)
+    if (args.seq[q].tile_base - base0 <= t_local) b = q;
+  const int kt = t_local - (args.seq[b].tile_base - base0);
+  const int L = args.seq[b].len;
+  const int start = args.seq[b].start;
+  const int G = args.seq[b].G;
+  const DivMagic gdiv{args.seq[b].gmul, args.seq[b].gshift};
+  const int Hkv = args.Hkv;
+  const uint16_t* __restrict__ Kp = (const uint16_t*)args.K;
+  const uint16_t* __restrict__ Vp = (const uint16_t*)args.V;
+  const float2* __restrict__ tab = args.tab;
+  uint8_t* rec = args.rec + ((size_t)g * args.tiles_total + args.seq[b].tile_base + kt) * kRecBytes;
+  uint16_t* kr = reinterpret_cast<uint16_t*>(rec);
+  uint16_t* kc = reinterpret_cast<uint16_t*>(rec + kRecKr);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(rec + kRecKr + kRecKc);
+
+  const int tid = threadIdx.x;
+  const int k = tid >> 3, p = tid & 7;  // key of the tile; pairs 8p .. 8p+7
+  const int j = kt * BK + k;
+  const bool valid = j < L;
+  const size_t row_off = ((size_t)(start + min(j, L - 1)) * Hkv + g) * D;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  {
+    const uint4 v0 = valid ? *reinterpret_cast<const uint4*>(Vp + row_off + 8 * p) : zero;
+    const uint4 v1 = valid ? *reinterpret_cast<const uint4*>(Vp + row_off + 64 + 8 * p) : zero;
+    *reinterpret_cast<uint4*>(&sv[k][8 * p]) = v0;
+    *reinterpret_cast<uint4*>(&sv[k][64 + 8 * p]) = v1;
+  }
+  if (G > 1) {  // G = 1: every pair is local, the remote copy is never read
+    uint4 y1p = zero, y2p = zero;
+    if (valid) {
+      const uint4 a = *reinterpret_cast<const uint4*>(Kp + row_off + 8 * p);
+      const uint4 c = *reinterpret_cast<const uint4*>(Kp + row_off + 64 + 8 * p);
+      const float4* trow =
+          reinterpret_cast<const float4*>(tab + (size_t)(j - alias_fast(j, gdiv)) * 64 + 8 * p);
+      float y1[8], y2[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float4 cs = trow[e2];
+        rot_neg(bf16_at(a, 2 * e2), bf16_at(c, 2 * e2), cs.x, cs.y, y1[2 * e2], y2[2 * e2]);
+        rot_neg(bf16_at(a, 2 * e2 + 1), bf16_at(c, 2 * e2 + 1), cs.z, cs.w, y1[2 * e2 + 1],
+                y2[2 * e2 + 1]);
+      }
+      y1p = make_uint4(pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
+                       pack_f16(y1[6], y1[7]));
+      y2p = make_uint4(pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]), pack_f16(y2[4], y2[5]),
+                       pack_f16(y2[6], y2[7]));
+    }
+    *reinterpret_cast<uint4*>(kr + k * D + 8 * p) = y1p;
+    *reinterpret_cast<uint4*>(kr + k * D + 64 + 8 * p) = y2p;
+    if (tid < 4 * BK) {
+      // hi/lo of selected pair cp of key ck: [lo ch0..7 | hi ch0..7], channel
+      // q = pair (q % 4), component (q / 4)
+      const int ck = tid >> 2, cp = tid & 3;
+      const int jc = kt * BK + ck;
+      uint32_t h1 = 0, l1 = 0, h2 = 0, l2 = 0;
+      if (jc < L) {
+        const int m = args.sel[g * kSelPairs + cp];
+        const uint16_t* row = Kp + ((size_t)(start + jc) * Hkv + g) * D;
+        const float2 cs = tab[(size_t)(jc - alias_fast(jc, gdiv)) * 64 + m];
+        float z1, z2;
+        rot_neg(__uint_as_float((uint32_t)row[m] << 16), __uint_as_float((uint32_t)row[m + 64] << 16),
+                cs.x, cs.y, z1, z2);
+        split_f16(z1, h1, l1);
+        split_f16(z2, h2, l2);
+      }
+      uint16_t* crow = kc + ck * 16;
+      crow[cp] = (uint16_t)l1;
+      crow[4 + cp] = (uint16_t)l2;
+      crow[8 + cp] = (uint16_t)h1;
+      crow[12 + cp] = (uint16_t)h2;
+    }
+  }
+  __syncthreads();
+  // V^T [d][key]: chunk c = (d, keys 8q .. 8q+7)
+#pragma unroll
+  for (int c = tid; c < D * BK / 8; c += 256) {
+    const int d = c >> 2, k8 = (c & 3) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)sv[k8 + 2 * q][d] | ((uint32_t)sv[k8 + 2 * q + 1][d] << 16);
+    *reinterpret_cast<uint4*>(vt + d * BK + k8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Main kernel
 // ---------------------------------------------------------------------------
 template <int REP>
@@ -258,92 +358,33 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
                  part[4] | (part[5] << 16), part[6] | (part[7] << 16)};
   };
 
-  // ---- K/V staging: global -> registers -> LDS --------------------------------------
-  // K: thread (key kr_ = tid/16, pair group kq = tid%16) holds channels 4kq..4kq+3 and
-  //    their RoPE partners 64+4kq..; V: thread (key pair vr = tid%16, chunk vc = tid/16)
-  //    holds channels 4vc..4vc+3 of keys 2vr, 2vr+1; the hi/lo correction of key tid/4,
-  //    pair tid%4 is done by the first 128 threads.
-  const int kr_ = tid >> 4, kq = tid & 15;
-  const int vr = tid & 15, vc = tid >> 4;
-  const int cr = (tid >> 2) & (BK - 1), cp = tid & 3;
-  const bool c_thread = tid < 4 * BK;
-  const int my_sel = args.sel[g * kSelPairs + cp];
-  uint2 kraw[2], vraw[2];
-  uint32_t ccor[2];   // selected pair (x1, x2) of key cr, pair my_sel, bf16 bits
-  float4 ktab[2];     // (cos, sin) of pairs 4kq .. 4kq+3 at n(key kr_) for the remote copy
-  float2 ctab;        // (cos, sin) of pair my_sel at n(key cr)
+  // ---- K/V staging: records / K rows -> registers -> LDS ------------------------------
+  // Every thread copies one 16-byte chunk of each array a tile needs: the remote keys
+  // and V^T from this head's tile record (512 chunks each), the 64 chunks of the hi/lo
+  // operand, and the standard keys of local and straddling tiles from K itself.
+  const uint8_t* rec_seq =
+      args.rec + ((size_t)g * args.tiles_total + args.seq[b].tile_base) * kRecBytes;
+  const uint16_t* kstd = Kp + ((size_t)start * Hkv + g) * D + 8 * (tid & 15);
+  uint4 r_kr, r_kc, r_vt, r_ks;
   auto stage_load = [&](int kt) __attribute__((always_inline)) {
-    const int j0 = kt * BK;
-    const bool remote_copy = kt < ktB;  // remote or straddling tile: rotate its keys
-    {
-      const int j = min(j0 + kr_, L - 1);
-      const uint16_t* row = Kp + ((size_t)(start + j) * Hkv + g) * D + 4 * kq;
-      kraw[0] = *reinterpret_cast<const uint2*>(row);
-      kraw[1] = *reinterpret_cast<const uint2*>(row + 64);
-      if (remote_copy) {
-        const float4* trow =
-            reinterpret_cast<const float4*>(tab + (size_t)(j - alias_fast(j, gdiv)) * 64 + 4 * kq);
-        ktab[0] = trow[0];
-        ktab[1] = trow[1];
-      }
+    const uint4* rec = reinterpret_cast<const uint4*>(rec_seq + (size_t)kt * kRecBytes);
+    if (kt < ktB) {  // remote or straddling tile
+      r_kr = rec[tid];
+      if (tid < 64) r_kc = rec[kRecKr / 16 + tid];
     }
-    if (c_thread && remote_copy) {
-      const int j = min(j0 + cr, L - 1);
-      const uint16_t* row = Kp + ((size_t)(start + j) * Hkv + g) * D;
-      ccor[0] = row[my_sel];
-      ccor[1] = row[my_sel + 64];
-      ctab = tab[(size_t)(j - alias_fast(j, gdiv)) * 64 + my_sel];
-    }
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int j = min(j0 + 2 * vr + k2, L - 1);
-      vraw[k2] = *reinterpret_cast<const uint2*>(Vp + ((size_t)(start + j) * Hkv + g) * D + 4 * vc);
+    r_vt = rec[(kRecKr + kRecKc) / 16 + tid];
+    if (kt >= ktA) {  // straddling or local tile
+      const int j = min(kt * BK + (tid >> 4), L - 1);
+      r_ks = *reinterpret_cast<const uint4*>(kstd + (size_t)j * Hkv * D);
     }
   };
   auto stage_store = [&](int kt, Stage& st) __attribute__((always_inline)) {
-    const int mode = kt < ktA ? kRemote : kt < ktB ? kStraddle : kLocal;
-    if (mode != kRemote) {
-      uint16_t* dst = st.ks + kr_ * KS_LD + 4 * kq;
-      *reinterpret_cast<uint2*>(dst) = kraw[0];
-      *reinterpret_cast<uint2*>(dst + 64) = kraw[1];
+    if (kt < ktB) {
+      *reinterpret_cast<uint4*>(st.kr + (tid >> 4) * KS_LD + 8 * (tid & 15)) = r_kr;
+      if (tid < 64) *reinterpret_cast<uint4*>(st.kc + (tid >> 1) * KC_LD + 8 * (tid & 1)) = r_kc;
     }
-    if (mode != kLocal) {
-      float y1[4], y2[4];
-      const float x1[4] = {bf16_lo(kraw[0].x), bf16_hi(kraw[0].x), bf16_lo(kraw[0].y),
-                           bf16_hi(kraw[0].y)};
-      const float x2[4] = {bf16_lo(kraw[1].x), bf16_hi(kraw[1].x), bf16_lo(kraw[1].y),
-                           bf16_hi(kraw[1].y)};
-      rot_neg(x1[0], x2[0], ktab[0].x, ktab[0].y, y1[0], y2[0]);
-      rot_neg(x1[1], x2[1], ktab[0].z, ktab[0].w, y1[1], y2[1]);
-      rot_neg(x1[2], x2[2], ktab[1].x, ktab[1].y, y1[2], y2[2]);
-      rot_neg(x1[3], x2[3], ktab[1].z, ktab[1].w, y1[3], y2[3]);
-      uint16_t* dst = st.kr + kr_ * KS_LD + 4 * kq;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]));
-      *reinterpret_cast<uint2*>(dst + 64) =
-          make_uint2(pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]));
-      // hi/lo of the selected pair cp for key cr: [lo ch0..7 | hi ch0..7],
-      // channel k = pair (k % 4), component (k / 4).
-      if (c_thread) {
-        float z1, z2;
-        rot_neg(__uint_as_float(ccor[0] << 16), __uint_as_float(ccor[1] << 16), ctab.x, ctab.y,
-                z1, z2);
-        uint32_t h1, l1, h2, l2;
-        split_f16(z1, h1, l1);
-        split_f16(z2, h2, l2);
-        uint16_t* row = st.kc + cr * KC_LD;
-        row[cp] = (uint16_t)l1;
-        row[4 + cp] = (uint16_t)l2;
-        row[8 + cp] = (uint16_t)h1;
-        row[12 + cp] = (uint16_t)h2;
-      }
-    }
-    // V^T: vt[d][key], keys (2vr, 2vr+1) packed per 32-bit word
-    uint32_t* dst = reinterpret_cast<uint32_t*>(st.vt) + vr;
-    const int d0 = 4 * vc;
-    dst[((d0 + 0) * VT_LD) / 2] = __byte_perm(vraw[0].x, vraw[1].x, 0x5410);
-    dst[((d0 + 1) * VT_LD) / 2] = __byte_perm(vraw[0].x, vraw[1].x, 0x7632);
-    dst[((d0 + 2) * VT_LD) / 2] = __byte_perm(vraw[0].y, vraw[1].y, 0x5410);
-    dst[((d0 + 3) * VT_LD) / 2] = __byte_perm(vraw[0].y, vraw[1].y, 0x7632);
+    if (kt >= ktA) *reinterpret_cast<uint4*>(st.ks + (tid >> 4) * KS_LD + 8 * (tid & 15)) = r_ks;
+    *reinterpret_cast<uint4*>(st.vt + (tid >> 2) * VT_LD + 8 * (tid & 3)) = r_vt;
   };
 
   // ---- softmax state and output accumulators --------------------------------------
@@ -512,7 +553,12 @@ static hipError_t launch_mfma_rep(const PrefillArgs& args, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs& args, hipStream_t stream) {
+hipError_t launch_prefill_mfma(const PrefillArgs& args, int chunk_tiles, hipStream_t stream) {
+  if (chunk_tiles > 0) {
+    hipLaunchKernelGGL(key_prep_kernel, dim3(chunk_tiles, args.Hkv), dim3(256), 0, stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   switch (args.Hq / args.Hkv) {
     case 1: return launch_mfma_rep<1>(args, stream);
     case 2: return launch_mfma_rep<2>(args, stream);

@@ -93,7 +93,10 @@ bf_status rope_apply(void* x, const int32_t* pos, int32_t pos0, int32_t T, int32
  *     Requires D = 128 and Hq/Hkv in {1, 2, 4, 8}.
  *   dt = BF_F32: float32 in/out and arithmetic (VALU); D in {64, 128}, any Hq/Hkv.
  *   ws, ws_bytes: workspace (device) of at least
- *     bifocal_workspace_bytes(BF_OP_PREFILL, max_b L_b, Hq, Hkv, D).
+ *     bifocal_workspace_bytes(BF_OP_PREFILL, max_b L_b, T, B, Hq, Hkv, D).  Besides the
+ *     position table it holds, for bf16, one record per KV head and 32-key tile (the
+ *     keys rotated to their aliased positions once per call, their hi/lo operand, and
+ *     V transposed), so its size grows with T.
  *   Errors: BF_EINVAL (null pointer, bad cu_seqlens, w0 < 1, ...), BF_EUNSUPPORTED,
  *           BF_EWORKSPACE; T = 0 is a no-op.
  */
@@ -117,7 +120,7 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
  *   o      (device) [Hq, D] output, dtype dt.   lse (device) [Hq] float32, or NULL.
  *   dt: BF_BF16 or BF_F32 for q, caches and o.  D in {64, 128}; Hq/Hkv in {1, 2, 4, 8}.
  *   ws, ws_bytes: workspace (device) of at least
- *     bifocal_workspace_bytes(BF_OP_DECODE, pos + 1, Hq, Hkv, D).
+ *     bifocal_workspace_bytes(BF_OP_DECODE, pos + 1, 0, 0, Hq, Hkv, D).
  *   Errors: BF_EINVAL (null pointer, pos < 0, w0 < 1, ...), BF_EUNSUPPORTED, BF_EWORKSPACE.
  */
 bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, void* o,
@@ -128,9 +131,13 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
 /*
  * bifocal_workspace_bytes -- workspace size for an operation.
  *   max_len: the longest sequence a prefill will see, or pos + 1 for decode.
+ *   total_tokens, num_seqs: prefill only, the largest T and B of the calls that will
+ *     use the workspace (max_len <= total_tokens <= num_seqs * max_len); ignored for
+ *     decode.
  *   Returns 0 for invalid arguments.
  */
-size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int32_t Hq, int32_t Hkv, int32_t D);
+size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int64_t total_tokens,
+                               int32_t num_seqs, int32_t Hq, int32_t Hkv, int32_t D);
 
 /* bifocal_status_string -- static text for a status code (never NULL). */
 const char* bifocal_status_string(int32_t status);

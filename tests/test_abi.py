@@ -57,12 +57,14 @@ def test_group_size_export(lib):
 
 
 def test_workspace_bytes(lib):
-    n = lib.bifocal_workspace_bytes(1, 131072, 32, 8, 128)
+    n = lib.bifocal_workspace_bytes(1, 131072, 131072, 1, 32, 8, 128)
     assert n >= 131072 * 64 * 8          # the position table alone
-    assert lib.bifocal_workspace_bytes(2, 131072, 32, 8, 128) > 0
-    assert lib.bifocal_workspace_bytes(1, 10, 3, 2, 128) == 0   # Hq % Hkv != 0
-    assert lib.bifocal_workspace_bytes(1, 10, 4, 2, 96) == 0    # unsupported D
-    assert lib.bifocal_workspace_bytes(7, 10, 4, 2, 128) == 0
+    assert lib.bifocal_workspace_bytes(2, 131072, 0, 0, 32, 8, 128) > 0
+    assert lib.bifocal_workspace_bytes(1, 10, 10, 1, 3, 2, 128) == 0   # Hq % Hkv != 0
+    assert lib.bifocal_workspace_bytes(1, 10, 10, 1, 4, 2, 96) == 0    # unsupported D
+    assert lib.bifocal_workspace_bytes(7, 10, 10, 1, 4, 2, 128) == 0
+    assert lib.bifocal_workspace_bytes(1, 10, 30, 2, 4, 2, 128) == 0   # T > B * max_len
+    assert lib.bifocal_workspace_bytes(1, 10, 5, 1, 4, 2, 128) == 0    # T < max_len
 
 
 def _prefill(lib, **kw):
