@@ -53,7 +53,9 @@ struct Stage {
   uint16_t vt[D * VT_LD];   // V^T, bf16 bits
 };
 constexpr int NSTAGE = 3;     // tile t computed while t+1 is scored and t+2 staged
-constexpr size_t kSmem = NSTAGE * sizeof(Stage);
+constexpr int QS_LD = D + 8;  // LDS row stride of a wave's standard query rows: 272 B
+constexpr size_t kQBytes = (size_t)NW * 32 * QS_LD * sizeof(uint16_t);
+constexpr size_t kSmem = NSTAGE * sizeof(Stage) + kQBytes;
 
 enum { kRemote = 0, kStraddle = 1, kLocal = 2 };
 }  // namespace mf
@@ -313,12 +315,19 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
 
   // ---- query operands -------------------------------------------------------------
   // B operand of S^T = K Q^T: lane (column ln, half hf) holds channels 16s + 8hf + e.
+  // The standard (bf16) rows also sit in this wave's LDS region, so that the switch to
+  // local tiles and the straddling tiles read LDS rather than global memory inside the
+  // loop (a global load there would make every tile wait for the staging loads).
   u32x4 qop[8];   // remote phase: fp16 of R(f(i)-i) q; local phase: bf16 q
   u32x4 qcor;     // hi (half 0) or lo (half 1) of the 8 selected remote channels
+  uint16_t* qlds = reinterpret_cast<uint16_t*>(smem_raw + NSTAGE * sizeof(Stage)) +
+                   (wave * 32 + ln) * QS_LD + 8 * hf;
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    *reinterpret_cast<uint4*>(qlds + 16 * s) = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hf);
   auto load_q_std = [&](u32x4* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      dst[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
+    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const u32x4*>(qlds + 16 * s);
   };
   auto load_q_remote = [&]() __attribute__((always_inline)) {
     const int n = qrow_i - alias_fast(qrow_i, gdiv);
