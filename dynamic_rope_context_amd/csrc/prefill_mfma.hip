@@ -41,23 +41,31 @@ constexpr int D = 128;
 constexpr int BK = 32;        // keys per tile (one 32-row MFMA block)
 constexpr int NW = 8;         // waves per workgroup (32 query rows each)
 constexpr int ROWS = 256;     // query rows (head, position) per workgroup
-constexpr int KS_LD = D + 8;  // LDS row stride (16-bit elements) of the K arrays: 272 B
-constexpr int VT_LD = BK + 8; // LDS row stride of transposed V: 80 B (conflict-free writes)
-constexpr int KC_LD = 16;     // LDS row of the hi/lo correction operand: 32 B
+constexpr int KS_LD = D + 8;  // LDS row stride (16-bit elements) of the key operand: 272 B
+// The key operand of a tile (remote fp16 copy or standard bf16 rows) occupies 32 rows
+// of 17 16-byte chunks (one chunk of padding per row keeps the 128-bit operand reads
+// conflict-free), filled by nine 1 KiB LDS-DMA transfers.
+constexpr int K_CHUNKS = BK * (KS_LD / 8);  // 544
+constexpr int K_DMA = 9;                    // 1 KiB transfers per key operand
+// V^T rows (one per channel d) hold the tile's 32 keys as four 16-byte chunks; chunk c
+// carries the keys one PV operand lane needs, {16t+4h .. +3, 16t+8+4h .. +3} for
+// c = 2t + h, and sits at position c ^ ((d >> 2) & 3) so that the 16 lanes served
+// together by a 128-bit LDS read hit 16 different bank groups.
+constexpr int VT_LD = BK;
+// hi/lo operand rows: 32 B = two chunks, chunk h at position h ^ ((key >> 3) & 1).
+constexpr int KC_LD = 16;
 constexpr float kLazy = 8.f;  // allowed growth of the running max before a rescale
 
 struct Stage {
-  uint16_t ks[BK * KS_LD];  // standard keys, bf16 bits
-  uint16_t kr[BK * KS_LD];  // remote keys R(f(j)-j) K_j, fp16 bits
+  uint16_t k[K_DMA * 512];  // key operand: remote fp16 or standard bf16, padded rows
   uint16_t kc[BK * KC_LD];  // [lo of 8 selected channels | hi of them], fp16 bits
-  uint16_t vt[D * VT_LD];   // V^T, bf16 bits
+  uint16_t vt[D * VT_LD];   // V^T, bf16 bits, swizzled chunks (see VT_LD)
 };
-constexpr int NSTAGE = 3;     // tile t computed while t+1 is scored and t+2 staged
-constexpr int QS_LD = D + 8;  // LDS row stride of a wave's standard query rows: 272 B
-constexpr size_t kQBytes = (size_t)NW * 32 * QS_LD * sizeof(uint16_t);
-constexpr size_t kSmem = NSTAGE * sizeof(Stage) + kQBytes;
+static_assert(sizeof(Stage) == 18432, "stage = 18 KiB");
+constexpr int NSTAGE = 6;          // LDS ring of virtual tiles
+constexpr int PREF = NSTAGE - 1;   // tiles issued ahead of the one being computed
+constexpr size_t kSmem = NSTAGE * sizeof(Stage);
 
-enum { kRemote = 0, kStraddle = 1, kLocal = 2 };
 }  // namespace mf
 
 // R(-n) with the table entry (cos, sin) of n: (x1, x2) -> (x1 c + x2 s, x2 c - x1 s).
@@ -234,40 +242,66 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
         split_f16(z2, h2, l2);
       }
       uint16_t* crow = kc + ck * 16;
-      crow[cp] = (uint16_t)l1;
-      crow[4 + cp] = (uint16_t)l2;
-      crow[8 + cp] = (uint16_t)h1;
-      crow[12 + cp] = (uint16_t)h2;
+      const int lo_at = 8 * ((ck >> 3) & 1), hi_at = 8 - lo_at;  // swizzled chunks
+      crow[lo_at + cp] = (uint16_t)l1;
+      crow[lo_at + 4 + cp] = (uint16_t)l2;
+      crow[hi_at + cp] = (uint16_t)h1;
+      crow[hi_at + 4 + cp] = (uint16_t)h2;
     }
   }
   __syncthreads();
-  // V^T [d][key]: chunk c = (d, keys 8q .. 8q+7)
+  // V^T [d][32 keys] in 16-byte chunks: physical chunk pc of row d holds logical chunk
+  // c = pc ^ ((d >> 2) & 3), i.e. keys {16t+4h .. +3, 16t+8+4h .. +3} with c = 2t + h.
 #pragma unroll
-  for (int c = tid; c < D * BK / 8; c += 256) {
-    const int d = c >> 2, k8 = (c & 3) * 8;
+  for (int q = tid; q < D * 4; q += 256) {
+    const int d = q >> 2, pc = q & 3;
+    const int c = pc ^ ((d >> 2) & 3);
+    const int k0 = 16 * (c >> 1) + 4 * (c & 1);
     uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = (uint32_t)sv[k8 + 2 * q][d] | ((uint32_t)sv[k8 + 2 * q + 1][d] << 16);
-    *reinterpret_cast<uint4*>(vt + d * BK + k8) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int e = 0; e < 2; ++e)
+      w[e] = (uint32_t)sv[k0 + 2 * e][d] | ((uint32_t)sv[k0 + 2 * e + 1][d] << 16);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      w[2 + e] = (uint32_t)sv[k0 + 8 + 2 * e][d] | ((uint32_t)sv[k0 + 8 + 2 * e + 1][d] << 16);
+    *reinterpret_cast<uint4*>(vt + d * BK + 8 * pc) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Main kernel
 // ---------------------------------------------------------------------------
+// Wait until at most N vector-memory operations of this wave are outstanding and all
+// its LDS operations are done, then meet the other waves.  Raw barrier: the ordinary
+// workgroup barrier also drains every LDS-DMA transfer in flight (vmcnt 0), which
+// would cut the prefetch depth to zero.  The empty asm statements keep the compiler
+// from moving memory operations across.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));  // vmcnt(N) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte LDS-DMA transfer per lane: lane l's 16 bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0,
+                                   0);
+}
+
 template <int REP>
 __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   using namespace mf;
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  Stage* stg = reinterpret_cast<Stage*>(smem_raw);
 
   constexpr int BMPOS = ROWS / REP;       // query positions per workgroup
   constexpr int PBLK = BMPOS / 32;        // 32-row position blocks per head
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;              // 0 .. NW-1: one 32-query block each
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0 .. NW-1
   const int ln = lane & 31;               // MFMA column / row within a 32-block
   const int hf = lane >> 5;               // lane half
 
@@ -292,7 +326,6 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
 
   const uint16_t* __restrict__ Qp = (const uint16_t*)args.Q;
   const uint16_t* __restrict__ Kp = (const uint16_t*)args.K;
-  const uint16_t* __restrict__ Vp = (const uint16_t*)args.V;
   const float2* __restrict__ tab = args.tab;
 
   // ---- this wave's 32-query block -------------------------------------------------
@@ -302,8 +335,13 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const uint16_t* qrow = Qp + ((size_t)(start + qrow_i) * Hq + qhead) * D;
 
   // ---- tile ranges --------------------------------------------------------------
+  // Physical key tiles [0,ktA) are remote for every query of the block, [ktB,nkt) local,
+  // [ktA,ktB) straddle the window edge.  The block walks a sequence of virtual tiles:
+  // a remote pass over [0,ktB), then a local pass over [ktA,nkt); on straddling tiles
+  // each pass masks the pairs of the other class, so every pair is scored once, by its
+  // own rule, in one online softmax.
   const int nkt = (i_end - 1) / BK + 1;
-  int ktA, ktB;  // [0,ktA) remote, [ktA,ktB) straddle, [ktB,nkt) local
+  int ktA, ktB;
   {
     const long long x = (long long)i0 - w0 - (BK - 1);
     ktA = x >= 0 ? (int)(x / BK) + 1 : 0;
@@ -312,22 +350,16 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     ktA = min(ktA, nkt);
     ktB = min(max(ktB, ktA), nkt);
   }
+  const int nvt = ktB + (nkt - ktA);
+  auto vt_kt = [&](int v) __attribute__((always_inline)) { return v < ktB ? v : ktA + (v - ktB); };
 
   // ---- query operands -------------------------------------------------------------
   // B operand of S^T = K Q^T: lane (column ln, half hf) holds channels 16s + 8hf + e.
-  // The standard (bf16) rows also sit in this wave's LDS region, so that the switch to
-  // local tiles and the straddling tiles read LDS rather than global memory inside the
-  // loop (a global load there would make every tile wait for the staging loads).
-  u32x4 qop[8];   // remote phase: fp16 of R(f(i)-i) q; local phase: bf16 q
+  u32x4 qop[8];   // remote pass: fp16 of R(f(i)-i) q; local pass: bf16 q
   u32x4 qcor;     // hi (half 0) or lo (half 1) of the 8 selected remote channels
-  uint16_t* qlds = reinterpret_cast<uint16_t*>(smem_raw + NSTAGE * sizeof(Stage)) +
-                   (wave * 32 + ln) * QS_LD + 8 * hf;
+  auto load_q_std = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    *reinterpret_cast<uint4*>(qlds + 16 * s) = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hf);
-  auto load_q_std = [&](u32x4* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const u32x4*>(qlds + 16 * s);
+    for (int s = 0; s < 8; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
   };
   auto load_q_remote = [&]() __attribute__((always_inline)) {
     const int n = qrow_i - alias_fast(qrow_i, gdiv);
@@ -367,78 +399,89 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
                  part[4] | (part[5] << 16), part[6] | (part[7] << 16)};
   };
 
-  // ---- K/V staging: records / K rows -> registers -> LDS ------------------------------
-  // Every thread copies one 16-byte chunk of each array a tile needs: the remote keys
-  // and V^T from this head's tile record (512 chunks each), the 64 chunks of the hi/lo
-  // operand, and the standard keys of local and straddling tiles from K itself.
+  // ---- staging: LDS-DMA straight from the key-tile records / K rows ----------------
+  // Wave w moves key-operand transfer w (wave 0 also transfer 8, the hi/lo operand of
+  // remote tiles) and V^T kilobyte w.  Lane l of key transfer i fills padded position
+  // p = 64 i + l: row p / 17, chunk p % 17 (chunk 16 and rows past 31 are padding and
+  // take a harmless dummy copy).  Every wave issues at least two transfers per virtual
+  // tile, which the vmcnt bound of the loop relies on.
   const uint8_t* rec_seq =
       args.rec + ((size_t)g * args.tiles_total + args.seq[b].tile_base) * kRecBytes;
-  const uint16_t* kstd = Kp + ((size_t)start * Hkv + g) * D + 8 * (tid & 15);
-  uint4 r_kr, r_kc, r_vt, r_ks;
-  auto stage_load = [&](int kt) __attribute__((always_inline)) {
-    const uint4* rec = reinterpret_cast<const uint4*>(rec_seq + (size_t)kt * kRecBytes);
-    if (kt < ktB) {  // remote or straddling tile
-      r_kr = rec[tid];
-      if (tid < 64) r_kc = rec[kRecKr / 16 + tid];
+  const uint16_t* kseq = Kp + ((size_t)start * Hkv + g) * D;
+  const uint32_t krow_stride = (uint32_t)Hkv * D;  // elements between tokens
+  int kpos_r[2], kpos_c[2];  // padded row / chunk of this lane in transfers wave, 8
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int p = 64 * (q == 0 ? wave : 8) + lane;
+    const int r = p / 17, c = p % 17;
+    const bool real = c < 16 && r < BK;
+    kpos_r[q] = real ? r : 0;
+    kpos_c[q] = real ? c : 0;
+  }
+  auto issue = [&](int v, int so) __attribute__((always_inline)) {
+    v = min(v, nvt - 1);  // past the end: repeat the last tile (keeps the vmcnt count)
+    const int kt = vt_kt(v);
+    uint8_t* st = smem_raw + so;
+    const uint8_t* rec = rec_seq + (size_t)kt * kRecBytes;
+    if (v < ktB) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (q == 0 || wave == 0)
+          dma16(rec + (kpos_r[q] * 16 + kpos_c[q]) * 16,
+                st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
+      if (wave == 0) dma16(rec + kRecKr + 16 * lane, st + offsetof(Stage, kc));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (q == 0 || wave == 0) {
+          const int j = min(kt * BK + kpos_r[q], L - 1);
+          dma16(kseq + (uint32_t)j * krow_stride + 8 * kpos_c[q],
+                st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
+        }
     }
-    r_vt = rec[(kRecKr + kRecKc) / 16 + tid];
-    if (kt >= ktA) {  // straddling or local tile
-      const int j = min(kt * BK + (tid >> 4), L - 1);
-      r_ks = *reinterpret_cast<const uint4*>(kstd + (size_t)j * Hkv * D);
-    }
+    dma16(rec + kRecKr + kRecKc + 1024 * wave + 16 * lane, st + offsetof(Stage, vt) + 1024 * wave);
   };
-  auto stage_store = [&](int kt, Stage& st) __attribute__((always_inline)) {
-    if (kt < ktB) {
-      *reinterpret_cast<uint4*>(st.kr + (tid >> 4) * KS_LD + 8 * (tid & 15)) = r_kr;
-      if (tid < 64) *reinterpret_cast<uint4*>(st.kc + (tid >> 1) * KC_LD + 8 * (tid & 1)) = r_kc;
-    }
-    if (kt >= ktA) *reinterpret_cast<uint4*>(st.ks + (tid >> 4) * KS_LD + 8 * (tid & 15)) = r_ks;
-    *reinterpret_cast<uint4*>(st.vt + (tid >> 2) * VT_LD + 8 * (tid & 3)) = r_vt;
-  };
+  constexpr int kStageBytes = (int)sizeof(Stage);
+  auto slot = [&](int v) __attribute__((always_inline)) { return (v % NSTAGE) * kStageBytes; };
 
   // ---- softmax state and output accumulators --------------------------------------
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};  // O^T blocks [d block]
   float m_run = -1e30f, l_run = 0.f;
   const float c2 = args.scale * 1.4426950408889634f;  // scale * log2(e)
 
-  // Scores S^T (32 keys x this wave's 32 queries) of tile kt, by tile class.
-  auto qk = [&](int kt, const Stage& st) __attribute__((always_inline)) -> f32x16 {
+  // Scores S^T (32 keys x this wave's 32 queries) of one virtual tile.
+  auto qk_remote = [&](int so) __attribute__((always_inline)) -> f32x16 {
+    const Stage& st = *reinterpret_cast<const Stage*>(smem_raw + so);
     f32x16 sacc = f32x16{};
-    const uint16_t* krow_s = st.ks + ln * KS_LD + 8 * hf;
-    const uint16_t* krow_r = st.kr + ln * KS_LD + 8 * hf;
-    if (kt >= ktB) {  // local
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        sacc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow_s + 16 * s), qop[s], sacc);
-      return sacc;
-    }
+    const uint16_t* krow = st.k + ln * KS_LD + 8 * hf;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      sacc = mfma_f16(*reinterpret_cast<const u32x4*>(krow_r + 16 * s), qop[s], sacc);
-    sacc = mfma_f16(*reinterpret_cast<const u32x4*>(st.kc + ln * KC_LD + 8 * hf), qcor, sacc);
-    if (kt >= ktA) {  // straddle: standard scores inside the window, selected per pair
-      u32x4 qs[8];
-      load_q_std(qs);
-      f32x16 sl = f32x16{};
+      sacc = mfma_f16(*reinterpret_cast<const u32x4*>(krow + 16 * s), qop[s], sacc);
+    const uint16_t* crow = st.kc + ln * KC_LD + 8 * (hf ^ ((ln >> 3) & 1));
+    return mfma_f16(*reinterpret_cast<const u32x4*>(crow), qcor, sacc);
+  };
+  auto qk_local = [&](int so) __attribute__((always_inline)) -> f32x16 {
+    const Stage& st = *reinterpret_cast<const Stage*>(smem_raw + so);
+    f32x16 sacc = f32x16{};
+    const uint16_t* krow = st.k + ln * KS_LD + 8 * hf;
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        sl = mfma_bf16(*reinterpret_cast<const u32x4*>(krow_s + 16 * s), qs[s], sl);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kt * BK + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (qi - j < w0) sacc[r] = sl[r];
-      }
-    }
+    for (int s = 0; s < 8; ++s)
+      sacc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 16 * s), qop[s], sacc);
     return sacc;
   };
 
-  // Online softmax of one tile's scores (in place -> probabilities) and O^T += V^T P^T.
-  auto softmax_pv = [&](int kt, f32x16 sacc, const Stage& st) __attribute__((always_inline)) {
-    if (kt * BK + BK - 1 > i0) {  // causal diagonal or ragged tail inside this tile
+  // Online softmax, part 1: masks, tile row max and the lazy rescale.  MK = 1: remote
+  // pass over a straddling tile, keep i - j >= w0.  MK = 2: local pass over a straddling
+  // or diagonal tile, keep 0 <= i - j < w0 (window and causality in one unsigned compare).
+  auto softmax_prep = [&](int v, f32x16& sacc, auto mk_c) __attribute__((always_inline)) {
+    constexpr int MK = decltype(mk_c)::value;
+    if constexpr (MK != 0) {
+      const int kt = vt_kt(v);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = kt * BK + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (j > qi || j >= L) sacc[r] = -INFINITY;
+        const bool drop = MK == 1 ? qi - j < w0 : (uint32_t)(qi - j) >= (uint32_t)w0;
+        if (drop) sacc[r] = -INFINITY;
       }
     }
     float mx = sacc[0];
@@ -455,8 +498,10 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       for (int db = 0; db < 4; ++db) oacc[db] *= f;
       m_run = m_new;
     }
+  };
+  // Part 2: probabilities in the PV operand layout (bf16) and the row-sum update.
+  auto softmax_exp = [&](const f32x16& sacc, uint32_t* pk) __attribute__((always_inline)) {
     const float mneg = -m_run;
-    uint32_t pk[8];
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -466,46 +511,73 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       pk[r / 2] = pack_bf16(p0, p1);
     }
     l_run += lsum;
+  };
+  // O^T += V^T P^T over the tile's 32 keys.
+  auto pv = [&](const uint32_t* pk, int so) __attribute__((always_inline)) {
+    const Stage& st = *reinterpret_cast<const Stage*>(smem_raw + so);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const u32x4 pb = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
-      const int kofs = 16 * t + 4 * hf;
+      const uint16_t* vrow = st.vt + ln * VT_LD + 8 * ((2 * t + hf) ^ ((ln >> 2) & 3));
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* vrow = st.vt + (32 * db + ln) * VT_LD + kofs;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        oacc[db] = mfma_bf16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, oacc[db]);
-      }
+      for (int db = 0; db < 4; ++db)
+        oacc[db] = mfma_bf16(*reinterpret_cast<const u32x4*>(vrow + 32 * VT_LD * db), pb, oacc[db]);
     }
   };
 
-  // ---- software-pipelined main loop ----------------------------------------------
-  // Iteration t: stage loads of tile t+2 are in flight, tile t+1 is scored (MFMA) while
-  // tile t goes through the softmax (VALU) and PV (MFMA), then tile t+2 is written to
-  // LDS.  Three LDS stages; one barrier per tile.
+  // ---- software-pipelined loop over virtual tiles ----------------------------------
+  // Iteration v: virtual tiles v+2 .. v+PREF are in flight (LDS-DMA), v+1 is scored
+  // (MFMA) while v goes through the softmax (VALU) and PV (MFMA).  Before the barrier
+  // closing iteration v, tile v+2 must have landed: the younger transfers (tiles v+3 ..
+  // v+PREF, at least two per tile) may still be in flight.
+  constexpr int kVmAhead = 2 * (PREF - 2);
   if (ktB > 0) load_q_remote();
-  else load_q_std(qop);
-  stage_load(0);
-  stage_store(0, stg[0]);
-  if (nkt > 1) {
-    stage_load(1);
-    stage_store(1, stg[1]);
-  }
-  __syncthreads();
-  f32x16 s_cur = qk(0, stg[0]);
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 2 < nkt) stage_load(kt + 2);
-    f32x16 s_next = f32x16{};
-    if (kt + 1 < nkt) {
-      if (kt + 1 == ktB && ktB > 0) load_q_std(qop);  // scores switch to local tiles
-      s_next = qk(kt + 1, stg[(kt + 1) % NSTAGE]);
-    }
-    softmax_pv(kt, s_cur, stg[kt % NSTAGE]);
-    if (kt + 2 < nkt) stage_store(kt + 2, stg[(kt + 2) % NSTAGE]);
-    __syncthreads();
+  else load_q_std();
+#pragma unroll
+  for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes);
+  wait_vm_barrier<kVmAhead>();  // tiles 0 and 1 in LDS
+  f32x16 s_cur = ktB > 0 ? qk_remote(0) : qk_local(0);
+
+  // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
+  // so its scores are computed unconditionally and simply unused past the end.
+  auto step = [&](int v, auto qkrem_c, auto mk_c) __attribute__((always_inline)) {
+    constexpr bool QKREM = decltype(qkrem_c)::value;  // class of tile v+1's scores
+    issue(v + PREF, slot(v + PREF));
+    const f32x16 s_next = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
+    softmax_prep(v, s_cur, mk_c);
+    uint32_t pk[8];
+    softmax_exp(s_cur, pk);
+    pv(pk, slot(v));
+    wait_vm_barrier<kVmAhead>();
     s_cur = s_next;
+  };
+  using kRem = std::true_type;
+  using kLoc = std::false_type;
+  using kNoMask = std::integral_constant<int, 0>;
+  using kRemMask = std::integral_constant<int, 1>;
+  using kLocMask = std::integral_constant<int, 2>;
+  // Phases of the virtual-tile walk (each loop body is specialised):
+  //   remote unmasked [0, ktA) | remote straddling [ktA, ktB) | local straddling
+  //   | local unmasked | local diagonal; the last remote tile switches the query operand.
+  const int kt_diag = i0 >= BK - 1 ? (i0 - (BK - 1)) / BK + 1 : 0;  // first diagonal tile
+  const int v_loc_plain = ktB + (ktB - ktA);           // first local tile past the window edge
+  const int v_diag = ktB + (max(kt_diag, ktA) - ktA);  // first local tile needing causality
+  int v = 0;
+  for (; v < min(ktA, ktB - 1); ++v) step(v, kRem(), kNoMask());
+  for (; v < ktB - 1; ++v) step(v, kRem(), kRemMask());
+  if (ktB > 0) {  // last remote tile: the next scores are local
+    load_q_std();
+    if (v >= ktA) step(v, kLoc(), kRemMask());
+    else step(v, kLoc(), kNoMask());
+    ++v;
   }
+  for (; v < min(v_loc_plain, nvt); ++v) step(v, kLoc(), kLocMask());
+  for (; v < v_diag; ++v) step(v, kLoc(), kNoMask());
+  for (; v < nvt; ++v) step(v, kLoc(), kLocMask());
+  // Transfers issued past the last tile must land before this workgroup's LDS is
+  // handed to another one.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
 
   // ---- epilogue: O = O^T / l, LSE ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
