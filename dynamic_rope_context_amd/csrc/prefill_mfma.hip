@@ -499,18 +499,23 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       m_run = m_new;
     }
   };
-  // Part 2: probabilities in the PV operand layout (bf16) and the row-sum update.
+  // Part 2: probabilities in the PV operand layout (bf16) and the row-sum update.  The
+  // row sum adds the same bf16-rounded probabilities that PV multiplies (two per
+  // v_dot2 against (1, 1), fp32 accumulation), so numerator and denominator agree.
   auto softmax_exp = [&](const f32x16& sacc, uint32_t* pk) __attribute__((always_inline)) {
     const float mneg = -m_run;
-    float lsum = 0.f;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float l0 = l_run, l1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = fast_exp2(__fmaf_rn(sacc[r], c2, mneg));
       const float p1 = fast_exp2(__fmaf_rn(sacc[r + 1], c2, mneg));
-      lsum += p0 + p1;
       pk[r / 2] = pack_bf16(p0, p1);
+      float& acc = (r & 2) ? l1 : l0;
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r / 2]), ones, acc,
+                                            false);
     }
-    l_run += lsum;
+    l_run = l0 + l1;
   };
   // O^T += V^T P^T over the tile's 32 keys.
   auto pv = [&](const uint32_t* pk, int so) __attribute__((always_inline)) {
@@ -539,17 +544,31 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   f32x16 s_cur = ktB > 0 ? qk_remote(0) : qk_local(0);
 
   // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
-  // so its scores are computed unconditionally and simply unused past the end.
-  auto step = [&](int v, auto qkrem_c, auto mk_c) __attribute__((always_inline)) {
+  // so its scores are computed unconditionally and simply unused past the end.  Two
+  // score register sets alternate between consecutive tiles (no copy per tile).
+  auto step = [&](int v, const f32x16& s_in, f32x16& s_out, auto qkrem_c, auto mk_c)
+      __attribute__((always_inline)) {
     constexpr bool QKREM = decltype(qkrem_c)::value;  // class of tile v+1's scores
     issue(v + PREF, slot(v + PREF));
-    const f32x16 s_next = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
-    softmax_prep(v, s_cur, mk_c);
+    s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
+    f32x16 sc = s_in;
+    softmax_prep(v, sc, mk_c);
     uint32_t pk[8];
-    softmax_exp(s_cur, pk);
+    softmax_exp(sc, pk);
     pv(pk, slot(v));
     wait_vm_barrier<kVmAhead>();
-    s_cur = s_next;
+  };
+  f32x16 s_alt;
+  auto run = [&](int& v, int end, auto qkrem_c, auto mk_c) __attribute__((always_inline)) {
+    for (; v + 1 < end; v += 2) {
+      step(v, s_cur, s_alt, qkrem_c, mk_c);
+      step(v + 1, s_alt, s_cur, qkrem_c, mk_c);
+    }
+    if (v < end) {
+      step(v, s_cur, s_alt, qkrem_c, mk_c);
+      s_cur = s_alt;
+      ++v;
+    }
   };
   using kRem = std::true_type;
   using kLoc = std::false_type;
@@ -563,17 +582,16 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const int v_loc_plain = ktB + (ktB - ktA);           // first local tile past the window edge
   const int v_diag = ktB + (max(kt_diag, ktA) - ktA);  // first local tile needing causality
   int v = 0;
-  for (; v < min(ktA, ktB - 1); ++v) step(v, kRem(), kNoMask());
-  for (; v < ktB - 1; ++v) step(v, kRem(), kRemMask());
+  run(v, min(ktA, ktB - 1), kRem(), kNoMask());
+  run(v, ktB - 1, kRem(), kRemMask());
   if (ktB > 0) {  // last remote tile: the next scores are local
     load_q_std();
-    if (v >= ktA) step(v, kLoc(), kRemMask());
-    else step(v, kLoc(), kNoMask());
-    ++v;
+    if (v >= ktA) run(v, v + 1, kLoc(), kRemMask());
+    else run(v, v + 1, kLoc(), kNoMask());
   }
-  for (; v < min(v_loc_plain, nvt); ++v) step(v, kLoc(), kLocMask());
-  for (; v < v_diag; ++v) step(v, kLoc(), kNoMask());
-  for (; v < nvt; ++v) step(v, kLoc(), kLocMask());
+  run(v, min(v_loc_plain, nvt), kLoc(), kLocMask());
+  run(v, v_diag, kLoc(), kNoMask());
+  run(v, nvt, kLoc(), kLocMask());
   // Transfers issued past the last tile must land before this workgroup's LDS is
   // handed to another one.
   asm volatile("" ::: "memory");
