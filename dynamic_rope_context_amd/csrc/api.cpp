@@ -258,14 +258,24 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
   bf_status s = ensure_table(ws, lay, D, theta, n_keys, st);
   if (s != BF_OK) return s;
 
-  // Split the cache so that ~2048 workgroups stream it; splits are whole multiples of
-  // 64 keys and their count a multiple of 8 (one slice per XCD).
-  int nsplit = (2048 + Hkv - 1) / Hkv;
-  nsplit = std::min(kDecodeMaxSplits, std::max(8, (nsplit + 7) / 8 * 8));
-  int kps = (n_keys + nsplit - 1) / nsplit;
-  kps = (kps + 63) / 64 * 64;
-  nsplit = (n_keys + kps - 1) / kps;
-  nsplit = (nsplit + 7) / 8 * 8;
+  int nsplit, kps;
+  if (dt == BF_BF16 && D == 128) {
+    // matrix-core kernel: one split per wave, 32-key blocks, four waves per workgroup;
+    // the split count is a multiple of 32 (whole workgroups, one slice per XCD)
+    kps = (n_keys + kDecodeMaxSplits - 1) / kDecodeMaxSplits;
+    kps = std::max(32, (kps + 31) / 32 * 32);
+    nsplit = (n_keys + kps - 1) / kps;
+    nsplit = (nsplit + 31) / 32 * 32;
+  } else {
+    // Split the cache so that ~2048 workgroups stream it; splits are whole multiples of
+    // 64 keys and their count a multiple of 8 (one slice per XCD).
+    nsplit = (2048 + Hkv - 1) / Hkv;
+    nsplit = std::min(kDecodeMaxSplits, std::max(8, (nsplit + 7) / 8 * 8));
+    kps = (n_keys + nsplit - 1) / nsplit;
+    kps = (kps + 63) / 64 * 64;
+    nsplit = (n_keys + kps - 1) / kps;
+    nsplit = (nsplit + 7) / 8 * 8;
+  }
   if (nsplit > kDecodeMaxSplits) return BF_EUNSUPPORTED;
 
   char* wsb = reinterpret_cast<char*>(ws);
@@ -285,6 +295,7 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
   a.gdiv = div_magic((uint32_t)a.G);
   a.nsplit = nsplit;
   a.kps = kps;
+  a.npart = (dt == BF_BF16 && D == 128) ? nsplit / 4 : nsplit;  // MFMA kernel merges 4 waves
   const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt((double)D);
   a.scale_log2 = (float)(scale * 1.4426950408889634);
   hipError_t e = launch_decode(a, rep, D, dt == BF_BF16, st);

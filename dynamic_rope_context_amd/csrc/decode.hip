@@ -253,36 +253,27 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the splits of each query head: O = sum_s w_s acc_s / sum_s w_s l_s with
+// Merge the partials of each query head: O = sum_s w_s acc_s / sum_s w_s l_s with
 // w_s = 2^(m_s - max m); LSE = ln 2 * (max m + log2 sum_s w_s l_s).  One workgroup per
-// query head; the splits are spread over the threads (the partials are read once).
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float u = __shfl_xor(v, o);
-    v = is_max ? fmaxf(v, u) : v + u;
-  }
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  v = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
-  return v;
-}
-
+// (query head, 32 channels): eight groups of 32 lanes sweep the partials, each lane one
+// channel, and meet in LDS.
 template <typename TOut, int D>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   __shared__ float s_w[kDecodeMaxSplits];
-  __shared__ float s_red[4];
-  __shared__ float s_o[256];
+  __shared__ float s_red[8][33];
   const int h = blockIdx.x;
+  const int d0 = 32 * blockIdx.y;
   const int tid = threadIdx.x;
-  const int ns = a.nsplit;
+  const int ns = a.npart;
   const float* base = a.part + (size_t)h * ns * (D + 2);
+  // max of the partial maxima (every thread scans a strided slice, then the block)
   float mx = -INFINITY;
   for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, base[(size_t)s * (D + 2) + D]);
-  mx = block_reduce(mx, true, s_red);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) s_red[tid >> 6][32] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0][32], s_red[1][32]), fmaxf(s_red[2][32], s_red[3][32]));
   float lsum = 0.f;
   for (int s = tid; s < ns; s += 256) {
     const float ms = base[(size_t)s * (D + 2) + D];
@@ -290,40 +281,51 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
     s_w[s] = w;
     lsum += w * base[(size_t)s * (D + 2) + D + 1];
   }
-  lsum = block_reduce(lsum, false, s_red);  // its barriers also publish s_w
-  constexpr int GROUPS = 256 / D;
-  const int d = tid % D, grp = tid / D;
-  float o = 0.f;
-#pragma unroll 8
-  for (int s = grp; s < ns; s += GROUPS) o += s_w[s] * base[(size_t)s * (D + 2) + d];
-  s_o[tid] = o;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+  __syncthreads();  // s_w complete, s_red[.][32] consumed
+  if ((tid & 63) == 0) s_red[tid >> 6][32] = lsum;
   __syncthreads();
-  if (tid < D) {
+  lsum = s_red[0][32] + s_red[1][32] + s_red[2][32] + s_red[3][32];
+  const int grp = tid >> 5, c = tid & 31;
+  float o = 0.f;
+  for (int s = grp; s < ns; s += 8) o += s_w[s] * base[(size_t)s * (D + 2) + d0 + c];
+  s_red[grp][c] = o;
+  __syncthreads();
+  if (tid < 32) {
     float v = 0.f;
 #pragma unroll
-    for (int q = 0; q < GROUPS; ++q) v += s_o[q * D + tid];
+    for (int q = 0; q < 8; ++q) v += s_red[q][tid];
     const float val = v / lsum;
     if constexpr (sizeof(TOut) == 2)
-      ((uint16_t*)a.o)[(size_t)h * D + tid] = (uint16_t)f32_to_bf16_bits(val);
+      ((uint16_t*)a.o)[(size_t)h * D + d0 + tid] = (uint16_t)f32_to_bf16_bits(val);
     else
-      ((float*)a.o)[(size_t)h * D + tid] = val;
-    if (a.lse && tid == 0) a.lse[h] = (mx + log2f(lsum)) * 0.69314718055994530942f;
+      ((float*)a.o)[(size_t)h * D + d0 + tid] = val;
+    if (a.lse && blockIdx.y == 0 && tid == 0) a.lse[h] = (mx + log2f(lsum)) * 0.69314718055994530942f;
   }
 }
 
+hipError_t launch_decode_mfma(const DecodeArgs& a, int rep, hipStream_t stream);
+
 template <typename TIn, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, int rep, hipStream_t stream) {
-  dim3 grid(a.nsplit * a.Hkv);
-  switch (rep) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 1>), grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 2>), grid, dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 4>), grid, dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 8>), grid, dim3(256), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (sizeof(TIn) == 2 && D == 128) {
+    // bf16 cache, D = 128: matrix-core split kernel (one split per wave)
+    hipError_t e = launch_decode_mfma(a, rep, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    dim3 grid(a.nsplit * a.Hkv);
+    switch (rep) {
+      case 1: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 1>), grid, dim3(256), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 2>), grid, dim3(256), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 4>), grid, dim3(256), 0, stream, a); break;
+      case 8: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 8>), grid, dim3(256), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<TIn, D>), dim3(a.Hq), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<TIn, D>), dim3(a.Hq, D / 32), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ struct DecodeArgs {
   float* part;         // [Hq][nsplit][D + 2] (acc..., m, l) in the base-2 domain
   void* o;             // [Hq, D]
   float* lse;          // [Hq] or null
-  int32_t pos, Hq, Hkv, w0, G, nsplit, kps;  // kps: keys per split (multiple of 64)
+  int32_t pos, Hq, Hkv, w0, G, nsplit, kps;  // kps: keys per split
+  int32_t npart;                             // partials per query head left for the combine
   DivMagic gdiv;                             // floor(x / G) without a divide
   float scale_log2;                          // softmax scale * log2(e)
 };

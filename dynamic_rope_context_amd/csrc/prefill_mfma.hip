@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "bf_common.h"
+#include "mfma_util.h"
 #include "prefill_args.h"
 
 namespace bifocal {
@@ -67,41 +68,6 @@ constexpr int PREF = NSTAGE - 1;   // tiles issued ahead of the one being comput
 constexpr size_t kSmem = NSTAGE * sizeof(Stage);
 
 }  // namespace mf
-
-// R(-n) with the table entry (cos, sin) of n: (x1, x2) -> (x1 c + x2 s, x2 c - x1 s).
-// Written with explicit roundings so that every caller gets identical bits.  The empty
-// asm pins the float32 results: without it the compiler may fold "fma, then convert to
-// fp16" into one mixed-precision FMA that rounds once, straight to fp16, at some call
-// sites and not at others, and the hi/lo split must see the very hi value the main
-// operand carries.
-__device__ __forceinline__ void rot_neg(float x1, float x2, float c, float s, float& y1,
-                                        float& y2) {
-  y1 = __fmaf_rn(x1, c, __fmul_rn(x2, s));
-  y2 = __fmaf_rn(x2, c, -__fmul_rn(x1, s));
-  asm volatile("" : "+v"(y1), "+v"(y2));
-}
-
-// fp16 hi part and the fp16 remainder, from the same conversion as the main remote
-// operands (pack_f16), so the correction completes exactly the hi value they carry.
-__device__ __forceinline__ void split_f16(float y, uint32_t& hi, uint32_t& lo) {
-  hi = f16_bits_of(y);
-  const float hf = (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
-  lo = f16_bits_of(y - hf);
-}
-
-__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf16_at(const uint4& w, int e) {
-  const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
-  return (e & 1) ? bf16_hi(x) : bf16_lo(x);
-}
 
 // ---------------------------------------------------------------------------
 // Pre-pass: per (head, RoPE pair) maximum of the squared pair norm over all tokens.
