@@ -43,9 +43,12 @@ def log(*a):
 KERNEL_SOURCES = {
     "prefill": ["dynamic_rope_context_amd/csrc/prefill_mfma.hip",
                 "dynamic_rope_context_amd/csrc/prefill_args.h",
+                "dynamic_rope_context_amd/csrc/mfma_util.h",
                 "dynamic_rope_context_amd/csrc/bf_common.h"],
-    "decode": ["dynamic_rope_context_amd/csrc/decode.hip",
+    "decode": ["dynamic_rope_context_amd/csrc/decode_mfma.hip",
+               "dynamic_rope_context_amd/csrc/decode.hip",
                "dynamic_rope_context_amd/csrc/decode_args.h",
+               "dynamic_rope_context_amd/csrc/mfma_util.h",
                "dynamic_rope_context_amd/csrc/bf_common.h"],
 }
 

@@ -262,8 +262,8 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
   if (dt == BF_BF16 && D == 128) {
     // matrix-core kernel: one split per wave, 32-key blocks, four waves per workgroup;
     // the split count is a multiple of 32 (whole workgroups, one slice per XCD)
-    kps = (n_keys + kDecodeMaxSplits - 1) / kDecodeMaxSplits;
-    kps = std::max(32, (kps + 31) / 32 * 32);
+    kps = (n_keys + 4 * kDecodeMaxSplits - 1) / (4 * kDecodeMaxSplits);
+    kps = std::max(kDecodeKeysPerWave, (kps + 31) / 32 * 32);
     nsplit = (n_keys + kps - 1) / kps;
     nsplit = (nsplit + 31) / 32 * 32;
   } else {
@@ -276,7 +276,9 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
     nsplit = (n_keys + kps - 1) / kps;
     nsplit = (nsplit + 7) / 8 * 8;
   }
-  if (nsplit > kDecodeMaxSplits) return BF_EUNSUPPORTED;
+  // partials left for the combine: one per workgroup (MFMA kernel) or per split
+  if ((dt == BF_BF16 && D == 128 ? nsplit / 4 : nsplit) > kDecodeMaxSplits)
+    return BF_EUNSUPPORTED;
 
   char* wsb = reinterpret_cast<char*>(ws);
   DecodeArgs a{};

@@ -46,7 +46,8 @@ struct WsLayout {
   int32_t n_cap;  // positions the table region can hold
 };
 
-constexpr int kDecodeMaxSplits = 512;
+constexpr int kDecodeMaxSplits = 512;     // partials per query head in the decode scratch
+constexpr int kDecodeKeysPerWave = 512;   // minimum keys a decode wave streams
 constexpr int kSelPairs = 4;  // RoPE pairs per KV head given the hi/lo correction
 constexpr size_t kKeyTileBytes = 17408;  // one prefill key-tile record (32 keys, D = 128)
 constexpr int kKeyTileKeys = 32;
@@ -97,6 +98,18 @@ inline size_t ws_bytes_for(int op, int max_len, int64_t total, int64_t num_seqs,
 // ---------------------------------------------------------------------------
 // Scalar helpers
 // ---------------------------------------------------------------------------
+
+// sin and cos of a float64 angle 0 <= a < 2^30: the angle is first reduced to
+// [-pi, pi] with a two-part 2*pi (Cody-Waite; the reduction error stays below 1e-11
+// for the position ranges used here), so the library routine takes its short path
+// instead of the large-argument reduction.
+__device__ __forceinline__ void sincos_reduced(double a, double* s, double* c) {
+  constexpr double kTwoPiHi = 6.283185307179586;
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;
+  const double k = rint(a * 0.15915494309189535);
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, a));
+  sincos(r, s, c);
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(256) rope_apply_kernel(T* __restrict__ x,
   const int p = pos ? pos[t] : pos0 + (int)t;
   const int f = alias_pos(p, G);
   double s64, c64;
-  sincos((double)f * inv_freq64(theta, m, D), &s64, &c64);
+  sincos_reduced((double)f * inv_freq64(theta, m, D), &s64, &c64);
   const float c = (float)c64, s = (float)s64;
   T* row = x + (size_t)t * H * D;
   for (int h = 0; h < H; ++h) {

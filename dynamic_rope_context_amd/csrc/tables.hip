@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(256) table_ensure_kernel(TableHeader* hdr, flo
     const int m = (int)(idx - (size_t)p * half);
     const double a = (double)p * inv_freq64(theta, m, D);
     double s, c;
-    sincos(a, &s, &c);
+    sincos_reduced(a, &s, &c);
     tab[idx] = make_float2((float)c, (float)s);
   }
 
