@@ -96,6 +96,8 @@ decode_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint16_t s_vt[NWD][D * BK];
   __shared__ __align__(16) uint16_t s_p[NWD][16 * BK];
   __shared__ __align__(16) uint16_t s_q[NWD][9 * D];
+  // table rows 0..15 (angles of the key offsets inside a block), rows padded by 16 B
+  __shared__ __align__(16) float2 s_dt[BK][64 + 2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -159,6 +161,12 @@ decode_mfma_kernel(DecodeArgs a) {
     }
   }
   const uint16_t* sq_row = s_q[wave] + (l16 < REP ? l16 : 8) * D + 8 * kq;
+  for (int i = threadIdx.x; i < BK * 32; i += 256) {  // rows <= pos are built
+    const int r = i >> 5, c = i & 31;
+    *reinterpret_cast<float4*>(&s_dt[r][2 * c]) =
+        reinterpret_cast<const float4*>(tab + (size_t)min(r, pos) * 64)[c];
+  }
+  __syncthreads();
 
   // ---- this wave's key range --------------------------------------------------------
   const int j_begin = wsplit * a.kps;
@@ -176,8 +184,8 @@ decode_mfma_kernel(DecodeArgs a) {
   }
 
   // Block loads, one block ahead: K (key l16, channels 32s + 8kq + e), V (keys 2kp,
-  // 2kp+1 of channel group cg = 16 channels) and, for blocks holding remote keys, the
-  // correction-table row of the key (pairs 32s + 8kq + e, s < 2).
+  // 2kp+1 of channel group cg = 16 channels) and the correction-table row of the key
+  // (pairs 32s + 8kq + e, s < 2).
   const int kp = lane & 7, cg = lane >> 3;
   struct Blk {
     uint4 k[4];
@@ -197,14 +205,18 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) x.v[k2][c] = *reinterpret_cast<const uint4*>(vr + 8 * c);
     }
-    if (j0 <= last_remote) {
-      const float4* tr =
-          reinterpret_cast<const float4*>(tab + (size_t)(jk - alias_fast(jk, a.gdiv)) * 64 + 8 * kq);
+    // The block's keys have consecutive n = j - f(j) (steps of 0 or 1): their angles
+    // are n0 + d with d < 16; the row of n0 is loaded here (one row per block, shared
+    // by all lanes), the rows of d sit in LDS.  Unconditional (unused for blocks
+    // without remote keys): a fixed number of loads per block lets every wait count
+    // only the loads it needs.
+    const int j0c = min(j0, pos);
+    const float4* tr =
+        reinterpret_cast<const float4*>(tab + (size_t)(j0c - alias_fast(j0c, a.gdiv)) * 64 + 8 * kq);
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) x.t[4 * s + e2] = tr[16 * s + e2];
-    }
+      for (int e2 = 0; e2 < 4; ++e2) x.t[4 * s + e2] = tr[16 * s + e2];
   };
 
   uint16_t* vt = s_vt[wave];
@@ -215,7 +227,9 @@ decode_mfma_kernel(DecodeArgs a) {
     const int jk = j0 + l16;
     const bool any_remote = j0 <= last_remote;
     const bool any_local = j0 + BK - 1 > last_remote;
-    if (b + 1 < nblk) load_blk(b + 1, nxt);
+    // unconditional (the last block reloads itself): a static count of loads in
+    // flight keeps the waits below from draining the prefetch
+    load_blk(min(b + 1, nblk - 1), nxt);
 
     // ---- V^T tile: keys (2kp, 2kp+1) of channels 16cg .. 16cg+15, one word each --------
     // row dd: four 8-byte segments of 4 keys; segment q sits at q ^ ((dd >> 2) & 3)
@@ -238,12 +252,19 @@ decode_mfma_kernel(DecodeArgs a) {
     // ---- scores S[h][key] -------------------------------------------------------------
     f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
     if (any_remote) {
+      const int j0c = min(j0, pos), jkc = min(jk, pos);
+      const int dk = (jkc - alias_fast(jkc, a.gdiv)) - (j0c - alias_fast(j0c, a.gdiv));
+      const float2* drow = &s_dt[dk][8 * kq];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         float y1[8], y2[8];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float4 cs = cur.t[4 * s + e2];
+          // R(n0 + d): compose the block row with the offset row
+          const float4 c0 = cur.t[4 * s + e2];
+          const float4 cd = *reinterpret_cast<const float4*>(drow + 32 * s + 2 * e2);
+          const float4 cs = make_float4(c0.x * cd.x - c0.y * cd.y, c0.y * cd.x + c0.x * cd.y,
+                                        c0.z * cd.z - c0.w * cd.w, c0.w * cd.z + c0.z * cd.w);
           rot_neg(bf16_at(cur.k[s], 2 * e2), bf16_at(cur.k[s + 2], 2 * e2), cs.x, cs.y,
                   y1[2 * e2], y2[2 * e2]);
           rot_neg(bf16_at(cur.k[s], 2 * e2 + 1), bf16_at(cur.k[s + 2], 2 * e2 + 1), cs.z, cs.w,
