@@ -15,7 +15,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = [
-    "lib", "lib_path", "rope_apply", "bifocal_prefill", "bifocal_decode", "workspace_bytes",
+    "lib", "lib_path", "rope_apply", "bifocal_prefill", "bifocal_decode", "bifocal_decode_batch",
+    "workspace_bytes",
     "group_size", "Workspace", "BifocalError", "OP_PREFILL", "OP_DECODE",
 ]
 
@@ -45,6 +46,9 @@ def _load():
     lib.bifocal_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f32,
                                    i32, vp, sz, vp]
     lib.bifocal_decode.restype = i32
+    lib.bifocal_decode_batch.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i32, f64, f32, i32, vp, sz, vp]
+    lib.bifocal_decode_batch.restype = i32
     lib.bifocal_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32]
     lib.bifocal_workspace_bytes.restype = sz
     lib.bifocal_status_string.argtypes = [i32]
@@ -199,4 +203,37 @@ def bifocal_decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, 
         _dev(lse, "lse") if lse is not None else 0, int(pos), Hq, Hkv, D, int(w0),
         int(w_pretrained), float(theta), float(softmax_scale), _dtype_code(q), workspace.ptr,
         workspace.nbytes, _stream(stream)), "bifocal_decode")
+    return out, lse
+
+
+def bifocal_decode_batch(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor,
+                         pos: Sequence[int], w0: int, w_pretrained: int, theta: float,
+                         softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                         workspace: Optional[Workspace] = None, stream=None
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One decode step per sequence of a ragged batch: q [B,Hq,D], sequence b at position
+    pos[b] over entries 0..pos[b] of Kcache/Vcache [B,S,Hkv,D] (standard RoPE), each with
+    its own G.  Returns (o [B,Hq,D], LSE [B,Hq] or None)."""
+    if q.dim() != 3 or Kcache.dim() != 4 or Vcache.shape != Kcache.shape:
+        raise BifocalError("expected q [B,Hq,D], Kcache and Vcache [B,S,Hkv,D]")
+    B, Hq, D = q.shape
+    S, Hkv = Kcache.shape[1], Kcache.shape[2]
+    pl = [int(p) for p in pos]
+    if len(pl) != B or Kcache.shape[0] != B or Kcache.shape[3] != D:
+        raise BifocalError("q, caches and pos disagree on the batch")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
+                                     num_seqs=max(B, 1))
+    pos_arr = (ctypes.c_int32 * max(B, 1))(*pl)
+    _check(lib().bifocal_decode_batch(
+        _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else 0, ctypes.cast(pos_arr, ctypes.c_void_p), B, S,
+        Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale),
+        _dtype_code(q), workspace.ptr, workspace.nbytes, _stream(stream)),
+        "bifocal_decode_batch")
     return out, lse

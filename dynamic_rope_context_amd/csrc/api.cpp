@@ -32,6 +32,7 @@ int prefill_f32_rows_per_block();
 int prefill_mfma_positions_per_block(int rep);
 
 hipError_t launch_decode(const DecodeArgs& a, int rep, int D, bool bf16, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeBatchArgs& a, int rep, hipStream_t stream);
 }  // namespace bifocal
 
 using namespace bifocal;
@@ -116,6 +117,7 @@ size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int64_t total_tokens
   if (op == BF_OP_PREFILL && (total_tokens < max_len || num_seqs < 1 ||
                               total_tokens > (int64_t)num_seqs * max_len))
     return 0;
+  if (op == BF_OP_DECODE && num_seqs < 0) return 0;
   return ws_bytes_for(op, max_len, total_tokens, num_seqs, Hq, Hkv, D);
 }
 
@@ -233,75 +235,142 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
   return BF_OK;
 }
 
-bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, void* o,
-                         float* lse, int32_t pos, int32_t Hq, int32_t Hkv, int32_t D, int32_t w0,
-                         int32_t w_pretrained, double theta, float softmax_scale, bf_dtype dt,
-                         void* ws, size_t ws_bytes, bf_stream stream) {
-  if (!q || !Kcache || !Vcache || !o || pos < 0 || pos == INT32_MAX || Hq < 1 || Hkv < 1 ||
-      Hq % Hkv || w0 < 1 || w_pretrained < 1 || !(theta > 0.0) || !std::isfinite(theta) ||
-      !std::isfinite(softmax_scale))
+}  // extern "C"
+
+namespace {
+
+// Shared by bifocal_decode (one sequence) and bifocal_decode_batch.
+bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse,
+                      const int32_t* pos, int32_t B, int64_t S, int32_t Hq, int32_t Hkv,
+                      int32_t D, int32_t w0, int32_t w_pretrained, double theta,
+                      float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
+                      bf_stream stream) {
+  if (B < 0 || (B > 0 && (!q || !Kcache || !Vcache || !o || !pos)) || S < 1 || Hq < 1 ||
+      Hkv < 1 || Hq % Hkv || w0 < 1 || w_pretrained < 1 || !(theta > 0.0) ||
+      !std::isfinite(theta) || !std::isfinite(softmax_scale))
     return BF_EINVAL;
   if (dt != BF_F32 && dt != BF_BF16) return BF_EINVAL;
   if (D != 64 && D != 128) return BF_EUNSUPPORTED;
   const int rep = Hq / Hkv;
   if (rep != 1 && rep != 2 && rep != 4 && rep != 8) return BF_EUNSUPPORTED;
+  int32_t max_pos = -1;
+  for (int32_t b = 0; b < B; ++b) {
+    if (pos[b] < 0 || pos[b] >= S) return BF_EINVAL;
+    max_pos = std::max(max_pos, pos[b]);
+  }
+  if (B == 0) return BF_OK;
   if (!aligned(q, 16) || !aligned(Kcache, 16) || !aligned(Vcache, 16) ||
       !aligned(o, dt == BF_BF16 ? 2 : 4) || (lse && !aligned(lse, 4)))
     return BF_EINVAL;
-  if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
-  const WsLayout lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes, 0);
-  const int32_t n_keys = pos + 1;
+  const int32_t n_keys = max_pos + 1;
   if (n_keys >= kMaxPositions) return BF_EUNSUPPORTED;
+  if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
+  const WsLayout lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes, 0, B);
   if (lay.scratch_off == 0 || lay.n_cap < n_keys) return BF_EWORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
+  char* wsb = reinterpret_cast<char*>(ws);
+  const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt((double)D);
+  const float scale_log2 = (float)(scale * 1.4426950408889634);
+  const size_t esz = dt == BF_BF16 ? 2 : 4;
+  const int64_t seq_stride = S * Hkv * D;  // elements
+
+  if (dt == BF_BF16 && D == 128) {
+    // Matrix-core kernel: angles evaluated in the kernel (no table), then the combine.
+    // Split count: about two workgroups per CU over the whole launch, at least eight
+    // 16-key blocks per wave when the sequences are long enough.
+    DecodeBatchArgs a{};
+    a.q = q;
+    a.K = Kcache;
+    a.V = Vcache;
+    a.part = reinterpret_cast<float*>(wsb + lay.scratch_off);
+    a.o = o;
+    a.lse = lse;
+    a.seq_stride = seq_stride;
+    a.theta = theta;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.w0 = w0;
+    a.scale_log2 = scale_log2;
+    for (int32_t b0 = 0; b0 < B; b0 += kDecodeMaxBatch) {
+      const int nb = std::min<int32_t>(kDecodeMaxBatch, B - b0);
+      int32_t mp = 0;
+      for (int i = 0; i < nb; ++i) mp = std::max(mp, pos[b0 + i]);
+      const int64_t nblk = mp / 16 + 1;
+      int64_t nwg = (512 + (int64_t)nb * Hkv - 1) / ((int64_t)nb * Hkv);
+      nwg = std::min<int64_t>(nwg, std::max<int64_t>(1, nblk / (4 * 8)));
+      nwg = std::max<int64_t>(1, std::min<int64_t>(nwg, kDecodeMaxParts));
+      a.b_base = b0;
+      a.nseq = nb;
+      a.nwg = (int32_t)nwg;
+      a.nsplit = (int32_t)nwg * 4;
+      for (int i = 0; i < nb; ++i) {
+        const int32_t G = group_size((int64_t)pos[b0 + i] + 1, w_pretrained);
+        const DivMagic m = div_magic((uint32_t)G);
+        a.seq[i] = DecSeq{pos[b0 + i], m.mul, m.shift, 0};
+      }
+      if (launch_decode_mfma(a, rep, st) != hipSuccess) return BF_EHIP;
+    }
+    return BF_OK;
+  }
+
+  // Vector path: one split launch + combine per sequence, sharing the table and the
+  // partials buffer (stream order).
   bf_status s = ensure_table(ws, lay, D, theta, n_keys, st);
   if (s != BF_OK) return s;
-
-  int nsplit, kps;
-  if (dt == BF_BF16 && D == 128) {
-    // matrix-core kernel: one split per wave, 32-key blocks, four waves per workgroup;
-    // the split count is a multiple of 32 (whole workgroups, one slice per XCD)
-    kps = (n_keys + 4 * kDecodeMaxSplits - 1) / (4 * kDecodeMaxSplits);
-    kps = std::max(kDecodeKeysPerWave, (kps + 31) / 32 * 32);
-    nsplit = (n_keys + kps - 1) / kps;
-    nsplit = (nsplit + 31) / 32 * 32;
-  } else {
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t nk = pos[b] + 1;
     // Split the cache so that ~2048 workgroups stream it; splits are whole multiples of
     // 64 keys and their count a multiple of 8 (one slice per XCD).
-    nsplit = (2048 + Hkv - 1) / Hkv;
+    int nsplit = (2048 + Hkv - 1) / Hkv;
     nsplit = std::min(kDecodeMaxSplits, std::max(8, (nsplit + 7) / 8 * 8));
-    kps = (n_keys + nsplit - 1) / nsplit;
+    int kps = (nk + nsplit - 1) / nsplit;
     kps = (kps + 63) / 64 * 64;
-    nsplit = (n_keys + kps - 1) / kps;
+    nsplit = (nk + kps - 1) / kps;
     nsplit = (nsplit + 7) / 8 * 8;
+    if (nsplit > kDecodeMaxSplits) return BF_EUNSUPPORTED;
+    DecodeArgs a{};
+    a.q = reinterpret_cast<const char*>(q) + (size_t)b * Hq * D * esz;
+    a.K = reinterpret_cast<const char*>(Kcache) + (size_t)b * seq_stride * esz;
+    a.V = reinterpret_cast<const char*>(Vcache) + (size_t)b * seq_stride * esz;
+    a.tab = reinterpret_cast<const float2*>(wsb + lay.table_off);
+    a.part = reinterpret_cast<float*>(wsb + lay.scratch_off);
+    a.o = reinterpret_cast<char*>(o) + (size_t)b * Hq * D * esz;
+    a.lse = lse ? lse + (size_t)b * Hq : nullptr;
+    a.pos = pos[b];
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.w0 = w0;
+    a.G = group_size((int64_t)pos[b] + 1, w_pretrained);
+    a.gdiv = div_magic((uint32_t)a.G);
+    a.nsplit = nsplit;
+    a.kps = kps;
+    a.scale_log2 = scale_log2;
+    if (launch_decode(a, rep, D, dt == BF_BF16, st) != hipSuccess) return BF_EHIP;
   }
-  // partials left for the combine: one per workgroup (MFMA kernel) or per split
-  if ((dt == BF_BF16 && D == 128 ? nsplit / 4 : nsplit) > kDecodeMaxSplits)
-    return BF_EUNSUPPORTED;
+  return BF_OK;
+}
 
-  char* wsb = reinterpret_cast<char*>(ws);
-  DecodeArgs a{};
-  a.q = q;
-  a.K = Kcache;
-  a.V = Vcache;
-  a.tab = reinterpret_cast<const float2*>(wsb + lay.table_off);
-  a.part = reinterpret_cast<float*>(wsb + lay.scratch_off);
-  a.o = o;
-  a.lse = lse;
-  a.pos = pos;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.w0 = w0;
-  a.G = group_size((int64_t)pos + 1, w_pretrained);
-  a.gdiv = div_magic((uint32_t)a.G);
-  a.nsplit = nsplit;
-  a.kps = kps;
-  a.npart = (dt == BF_BF16 && D == 128) ? nsplit / 4 : nsplit;  // MFMA kernel merges 4 waves
-  const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt((double)D);
-  a.scale_log2 = (float)(scale * 1.4426950408889634);
-  hipError_t e = launch_decode(a, rep, D, dt == BF_BF16, st);
-  return e == hipSuccess ? BF_OK : BF_EHIP;
+}  // namespace
+
+extern "C" {
+
+bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, void* o,
+                         float* lse, int32_t pos, int32_t Hq, int32_t Hkv, int32_t D, int32_t w0,
+                         int32_t w_pretrained, double theta, float softmax_scale, bf_dtype dt,
+                         void* ws, size_t ws_bytes, bf_stream stream) {
+  if (pos < 0 || pos == INT32_MAX) return BF_EINVAL;
+  return decode_impl(q, Kcache, Vcache, o, lse, &pos, 1, (int64_t)pos + 1, Hq, Hkv, D, w0,
+                     w_pretrained, theta, softmax_scale, dt, ws, ws_bytes, stream);
+}
+
+bf_status bifocal_decode_batch(const void* q, const void* Kcache, const void* Vcache, void* o,
+                               float* lse, const int32_t* pos, int32_t B, int32_t S, int32_t Hq,
+                               int32_t Hkv, int32_t D, int32_t w0, int32_t w_pretrained,
+                               double theta, float softmax_scale, bf_dtype dt, void* ws,
+                               size_t ws_bytes, bf_stream stream) {
+  return decode_impl(q, Kcache, Vcache, o, lse, pos, B, S, Hq, Hkv, D, w0, w_pretrained, theta,
+                     softmax_scale, dt, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -46,8 +46,8 @@ struct WsLayout {
   int32_t n_cap;  // positions the table region can hold
 };
 
-constexpr int kDecodeMaxSplits = 512;     // partials per query head in the decode scratch
-constexpr int kDecodeKeysPerWave = 512;   // minimum keys a decode wave streams
+constexpr int kDecodeMaxSplits = 512;     // partials per query head (vector decode path)
+constexpr int kDecodeMaxParts = 128;      // partials per (sequence, query head), matrix-core path
 constexpr int kSelPairs = 4;  // RoPE pairs per KV head given the hi/lo correction
 constexpr size_t kKeyTileBytes = 17408;  // one prefill key-tile record (32 keys, D = 128)
 constexpr int kKeyTileKeys = 32;
@@ -55,9 +55,15 @@ constexpr int kKeyTileKeys = 32;
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline size_t table_row_bytes(int D) { return (size_t)(D / 2) * 2 * sizeof(float); }
 
-// Op scratch: decode partials, or prefill pair maxima + selected pairs.
-inline size_t scratch_bytes(int op, int Hq, int Hkv, int D) {
-  if (op == 2) return align_up((size_t)Hq * kDecodeMaxSplits * (D + 2) * sizeof(float), 256);
+// Op scratch: decode partials (the larger of one sequence's vector path partials and
+// nseq sequences' matrix-core partials), or prefill pair maxima + selected pairs.
+inline size_t scratch_bytes(int op, int Hq, int Hkv, int D, int64_t nseq = 1) {
+  if (op == 2) {
+    if (nseq < 1) nseq = 1;
+    const size_t vec = (size_t)Hq * kDecodeMaxSplits * (D + 2) * sizeof(float);
+    const size_t mfma = (size_t)nseq * Hq * kDecodeMaxParts * (D + 2) * sizeof(float);
+    return align_up(vec > mfma ? vec : mfma, 256);
+  }
   if (op == 1) {
     const size_t mx = align_up((size_t)(Hq + Hkv) * 64 * sizeof(uint32_t), 256);
     return mx + align_up((size_t)Hkv * kSelPairs * sizeof(int32_t), 256);
@@ -74,10 +80,11 @@ inline int64_t max_tiles(int64_t total, int64_t num_seqs) {
   return (total + kKeyTileKeys - 1) / kKeyTileKeys + num_seqs;
 }
 
-inline WsLayout ws_layout(int op, int Hq, int Hkv, int D, size_t ws_bytes, size_t rec_bytes) {
+inline WsLayout ws_layout(int op, int Hq, int Hkv, int D, size_t ws_bytes, size_t rec_bytes,
+                          int64_t nseq = 1) {
   WsLayout l;
   l.table_off = 256;
-  l.scratch_bytes = scratch_bytes(op, Hq, Hkv, D);
+  l.scratch_bytes = scratch_bytes(op, Hq, Hkv, D, nseq);
   const size_t ws = ws_bytes / 256 * 256;
   const size_t tail = l.scratch_bytes + rec_bytes;
   l.scratch_off = ws > tail ? ws - l.scratch_bytes : 0;
@@ -92,7 +99,7 @@ inline size_t ws_bytes_for(int op, int max_len, int64_t total, int64_t num_seqs,
                            int D) {
   const size_t rec = op == 1 ? records_bytes(Hkv, max_tiles(total, num_seqs)) : 0;
   return 256 + align_up((size_t)max_len * table_row_bytes(D), 256) + rec +
-         scratch_bytes(op, Hq, Hkv, D);
+         scratch_bytes(op, Hq, Hkv, D, op == 2 ? num_seqs : 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,4 +1,6 @@
-// Bifocal decode: one query at position pos over a standard-RoPE KV cache (gfx950).
+// Bifocal decode, vector path (fp32 caches, and D = 64): one query at position pos over
+// a standard-RoPE KV cache (gfx950).  bf16 caches with D = 128 take the matrix-core
+// kernel instead.
 //
 // Jet-Long technical summary, "Methodology" section 2 (on-the-fly correction
 // rotation): the cache keeps keys with standard RoPE at their exact positions and is
@@ -19,7 +21,6 @@
 #include "decode_args.h"
 
 namespace bifocal {
-
 
 // DPP row rotation within 16-lane rows.
 template <int N>
@@ -264,7 +265,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x;
   const int d0 = 32 * blockIdx.y;
   const int tid = threadIdx.x;
-  const int ns = a.npart;
+  const int ns = a.nsplit;
   const float* base = a.part + (size_t)h * ns * (D + 2);
   // max of the partial maxima (every thread scans a strided slice, then the block)
   float mx = -INFINITY;
@@ -305,26 +306,18 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int rep, hipStream_t stream);
-
 template <typename TIn, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, int rep, hipStream_t stream) {
-  if constexpr (sizeof(TIn) == 2 && D == 128) {
-    // bf16 cache, D = 128: matrix-core split kernel (one split per wave)
-    hipError_t e = launch_decode_mfma(a, rep, stream);
-    if (e != hipSuccess) return e;
-  } else {
-    dim3 grid(a.nsplit * a.Hkv);
-    switch (rep) {
-      case 1: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 1>), grid, dim3(256), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 2>), grid, dim3(256), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 4>), grid, dim3(256), 0, stream, a); break;
-      case 8: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 8>), grid, dim3(256), 0, stream, a); break;
-      default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  dim3 grid(a.nsplit * a.Hkv);
+  switch (rep) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 1>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 2>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 4>), grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_split_kernel<TIn, D, 8>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<TIn, D>), dim3(a.Hq, D / 32), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -1,12 +1,14 @@
-// Bifocal decode on gfx950 matrix cores: one query at position pos, bf16 cache, D = 128.
+// Bifocal decode on gfx950 matrix cores: a batch of queries, one per sequence, over
+// bf16 standard-RoPE caches, D = 128.
 //
 // Jet-Long technical summary, "Methodology" section 2 (on-the-fly correction
 // rotation): the cache keeps keys with standard RoPE at their exact positions and is
 // never rewritten.  A remote key j is scored against R(f(j) - j) K_j, i.e. the stored
-// key rotated in fp32 registers by the table entry at n = j - f(j), and the query
-// rotated once by R(f(pos) - pos); rotations compose additively, so this is RoPE at the
-// aliased positions f(x) = floor(x/G) of section 1.  Keys inside the window (pos - j <
-// w0) are scored with the stored bytes as they are.
+// key rotated in fp32 registers by the angles of n = j - f(j), and the query rotated
+// once by R(f(pos) - pos); rotations compose additively, so this is RoPE at the
+// aliased positions f(x) = floor(x/G) of section 1, with G from the sequence's current
+// length pos + 1.  Keys inside the window (pos - j < w0) are scored with the stored
+// bytes as they are.
 //
 // Layout (per wave, 16 keys per block, 16x16 matrix-core shapes):
 //   * S = Q K^T with the query heads as MFMA rows and the block's keys as columns
@@ -16,15 +18,24 @@
 //   * Remote scores need fp32 accuracy (the fp32 rotation is not representable in one
 //     16-bit operand): keys and query are split into fp16 hi + lo parts and three
 //     MFMAs add hi*hi + hi*lo + lo*hi (the lo*lo term is below fp32 rounding).
+//   * Angles: the keys of a block have consecutive n = j - f(j) (steps of 0 or 1), so
+//     R(n) = R(n0) R(n - n0) with n - n0 < 16.  Each lane of a wave owns one RoPE pair
+//     and evaluates cos/sin(n0 theta_m) in fp64 once per block (rounded once to fp32,
+//     the values a precomputed table would hold); the 16 offset rows R(d) are built
+//     once per workgroup.  No table is read, so decode needs no table in the workspace.
 //   * O^T = V^T P^T (v_mfma_f32_16x16x16_bf16): the block's V rows are transposed
 //     through a per-wave LDS tile (pairs of keys packed per 32-bit word), P goes
 //     through a small LDS row buffer.
 //   * Online softmax in the base-2 domain with a lazy running max per head.
 //   * Two waves per SIMD (at most 256 registers each) so that one wave's loads are in
 //     flight while the other computes.
-// Each wave streams its own contiguous range of keys; the four waves of a workgroup
-// merge their states in LDS and write one partial (acc[D], m, l) per query head, and
-// decode_combine_kernel merges the workgroups.
+// Key blocks are dealt to the waves of a (sequence, KV head) round-robin: at any time
+// the waves of the whole grid read one contiguous window of the caches, which keeps
+// the DRAM access pattern a sweep.  The four waves of a workgroup merge their states
+// in LDS and write one partial (acc[D], m, l) per query head; a second kernel merges
+// the partials of each head by their log-sum-exp and writes O and LSE.  (Merging in
+// the last workgroup to finish instead puts a chain of uncached round trips at the end
+// of the grid, which measured slower than the second launch.)
 #include "bf_common.h"
 #include "decode_args.h"
 #include "mfma_util.h"
@@ -33,7 +44,7 @@ namespace bifocal {
 
 namespace dm {
 constexpr int D = 128;
-constexpr int BKD = 32;          // keys per block
+constexpr int BK = 16;           // keys per block
 constexpr int NWD = 4;           // waves per workgroup (one split each)
 constexpr float kLazy = 8.f;     // allowed growth of the running max before a rescale
 }  // namespace dm
@@ -86,49 +97,63 @@ __device__ __forceinline__ float row_sum(float x) {
   return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));
 }
 
+// fp32 (cos, sin) of n * theta_m, rounded once from fp64.
+__device__ __forceinline__ float2 angle_cs(int n, double invf) {
+  double s, c;
+  sincos_reduced((double)n * invf, &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
 template <int REP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-decode_mfma_kernel(DecodeArgs a) {
+decode_mfma_kernel(DecodeBatchArgs a) {
   using namespace dm;
-  constexpr int BK = 16;  // keys per block
   // per wave: V^T tile [128 channels][16 keys] (8-byte segments swizzled by row), P^T
-  // rows [16 heads][16 keys], standard query rows [8 heads][128] + one zero row
+  // rows [16 heads][16 keys], standard query rows [8 heads][128] + one zero row, and
+  // the angle row R(n0) of the current block (lane = RoPE pair)
   __shared__ __align__(16) uint16_t s_vt[NWD][D * BK];
   __shared__ __align__(16) uint16_t s_p[NWD][16 * BK];
   __shared__ __align__(16) uint16_t s_q[NWD][9 * D];
-  // table rows 0..15 (angles of the key offsets inside a block), rows padded by 16 B
+  __shared__ __align__(16) float2 s_row[NWD][64];
+  // offset rows R(d), d = 0..15, padded by 16 B
   __shared__ __align__(16) float2 s_dt[BK][64 + 2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, kq = lane >> 4;  // MFMA column / row, K group
 
-  // Workgroup -> (KV head, group of NWD splits); consecutive workgroups go to different
-  // XCDs and the splits of one XCD cover a contiguous key range for every head, so the
-  // table rows of that range are fetched into one L2 and shared by all heads.
-  const int nwg = a.nsplit / NWD;     // workgroups per head (multiple of 8)
-  const int per_xcd = nwg >> 3;
+  // Workgroup -> (sequence, group of NWD splits, KV head)
   const int id = blockIdx.x;
-  const int xcd = id & 7;
-  const int k_in = id >> 3;
-  const int g = k_in % a.Hkv;
-  const int wsplit = (xcd * per_xcd + k_in / a.Hkv) * NWD + wave;
+  const int g = id % a.Hkv;
+  const int wgi = (id / a.Hkv) % a.nwg;
+  const int bl = id / (a.Hkv * a.nwg);
+  const int b = a.b_base + bl;
+  const int w = wgi * NWD + wave;  // this wave's split
+  const int pos = a.seq[bl].pos;
+  const DivMagic gdiv{a.seq[bl].gmul, a.seq[bl].gshift};
+  const int nblk = pos / BK + 1;  // blocks holding keys 0 .. pos
+  const int nsplit = a.nsplit;
+  // this wave's blocks: w, w + nsplit, w + 2 nsplit, ... < nblk
+  const int cnt = w < nblk ? (nblk - 1 - w) / nsplit + 1 : 0;
 
-  const int pos = a.pos;
   const int last_remote = pos - a.w0;  // keys j <= last_remote are remote
   const float c2 = a.scale_log2;
-  const uint16_t* __restrict__ Kp = (const uint16_t*)a.K;
-  const uint16_t* __restrict__ Vp = (const uint16_t*)a.V;
-  const float2* __restrict__ tab = a.tab;
   const uint32_t rs = (uint32_t)a.Hkv * D;  // elements between consecutive cache rows
-  const uint16_t* kg = Kp + (size_t)g * D;
-  const uint16_t* vg = Vp + (size_t)g * D;
+  const uint16_t* kg = (const uint16_t*)a.K + (size_t)b * a.seq_stride + (size_t)g * D;
+  const uint16_t* vg = (const uint16_t*)a.V + (size_t)b * a.seq_stride + (size_t)g * D;
+  const double invf = inv_freq64(a.theta, lane, D);  // lane = RoPE pair
+  float2* row = s_row[wave];
+
+  // ---- angles: offset rows (shared) and the query's row --------------------------------
+#pragma unroll
+  for (int r = wave; r < BK; r += NWD) s_dt[r][lane] = angle_cs(r, invf);
+  row[lane] = angle_cs(pos - alias_fast(pos, gdiv), invf);
 
   // ---- query operands (A: rows = query heads, lanes l16 >= REP zero) ------------------
   // lane (head l16, group kq) holds channels 32s + 8kq + e, s = 0..3
   u32x4 qh[4], ql[4];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + (size_t)(g * REP + min(l16, REP - 1)) * D;
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)b * a.Hq + g * REP + min(l16, REP - 1)) * D;
     uint4 raw[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -143,11 +168,10 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         *reinterpret_cast<uint4*>(sq + 8 * D + 32 * s + 8 * kq) = make_uint4(0u, 0u, 0u, 0u);
-    const int nq = pos - alias_fast(pos, a.gdiv);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float y1[8], y2[8];
-      const float4* tr = reinterpret_cast<const float4*>(tab + (size_t)nq * 64 + 32 * s + 8 * kq);
+      const float4* tr = reinterpret_cast<const float4*>(row + 32 * s + 8 * kq);
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const float4 cs = tr[e2];
@@ -161,17 +185,7 @@ decode_mfma_kernel(DecodeArgs a) {
     }
   }
   const uint16_t* sq_row = s_q[wave] + (l16 < REP ? l16 : 8) * D + 8 * kq;
-  for (int i = threadIdx.x; i < BK * 32; i += 256) {  // rows <= pos are built
-    const int r = i >> 5, c = i & 31;
-    *reinterpret_cast<float4*>(&s_dt[r][2 * c]) =
-        reinterpret_cast<const float4*>(tab + (size_t)min(r, pos) * 64)[c];
-  }
-  __syncthreads();
-
-  // ---- this wave's key range --------------------------------------------------------
-  const int j_begin = wsplit * a.kps;
-  const int j_end = min(j_begin + a.kps, pos + 1);
-  const int nblk = j_end > j_begin ? (j_end - j_begin + BK - 1) / BK : 0;
+  __syncthreads();  // offset rows complete
 
   f32x4 oacc[8];  // O^T blocks [16 channels][16 head columns]
 #pragma unroll
@@ -183,17 +197,16 @@ decode_mfma_kernel(DecodeArgs a) {
     l_run[r] = 0.f;
   }
 
-  // Block loads, one block ahead: K (key l16, channels 32s + 8kq + e), V (keys 2kp,
-  // 2kp+1 of channel group cg = 16 channels) and the correction-table row of the key
-  // (pairs 32s + 8kq + e, s < 2).
+  // Block loads, one block ahead: K (key l16, channels 32s + 8kq + e) and V (keys 2kp,
+  // 2kp+1 of channel group cg = 16 channels).  Keys past pos are clamped to pos (their
+  // scores are masked).
   const int kp = lane & 7, cg = lane >> 3;
   struct Blk {
     uint4 k[4];
     uint4 v[2][2];
-    float4 t[8];
   };
-  auto load_blk = [&](int b, Blk& x) __attribute__((always_inline)) {
-    const int j0 = j_begin + b * BK;
+  auto load_blk = [&](int i, Blk& x) __attribute__((always_inline)) {
+    const int j0 = (w + i * nsplit) * BK;
     const int jk = min(j0 + l16, pos);
     const uint16_t* kr = kg + (uint32_t)jk * rs + 8 * kq;
 #pragma unroll
@@ -205,31 +218,19 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) x.v[k2][c] = *reinterpret_cast<const uint4*>(vr + 8 * c);
     }
-    // The block's keys have consecutive n = j - f(j) (steps of 0 or 1): their angles
-    // are n0 + d with d < 16; the row of n0 is loaded here (one row per block, shared
-    // by all lanes), the rows of d sit in LDS.  Unconditional (unused for blocks
-    // without remote keys): a fixed number of loads per block lets every wait count
-    // only the loads it needs.
-    const int j0c = min(j0, pos);
-    const float4* tr =
-        reinterpret_cast<const float4*>(tab + (size_t)(j0c - alias_fast(j0c, a.gdiv)) * 64 + 8 * kq);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) x.t[4 * s + e2] = tr[16 * s + e2];
   };
 
   uint16_t* vt = s_vt[wave];
   uint16_t* pt = s_p[wave];
   // Blocks alternate between two load buffers (no register copy between blocks).
-  auto block = [&](int b, const Blk& cur, Blk& nxt) __attribute__((always_inline)) {
-    const int j0 = j_begin + b * BK;
+  auto block = [&](int i, const Blk& cur, Blk& nxt) __attribute__((always_inline)) {
+    const int j0 = (w + i * nsplit) * BK;  // <= pos
     const int jk = j0 + l16;
     const bool any_remote = j0 <= last_remote;
     const bool any_local = j0 + BK - 1 > last_remote;
     // unconditional (the last block reloads itself): a static count of loads in
     // flight keeps the waits below from draining the prefetch
-    load_blk(min(b + 1, nblk - 1), nxt);
+    load_blk(min(i + 1, cnt - 1), nxt);
 
     // ---- V^T tile: keys (2kp, 2kp+1) of channels 16cg .. 16cg+15, one word each --------
     // row dd: four 8-byte segments of 4 keys; segment q sits at q ^ ((dd >> 2) & 3)
@@ -238,11 +239,11 @@ decode_mfma_kernel(DecodeArgs a) {
       const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&cur.v[0][c]);
       const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&cur.v[1][c]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int ww = 0; ww < 4; ++ww) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int dd = 16 * cg + 8 * c + 2 * w + hh;
-          const uint32_t word = __byte_perm(a0[w], a1[w], hh ? 0x7632 : 0x5410);
+          const int dd = 16 * cg + 8 * c + 2 * ww + hh;
+          const uint32_t word = __byte_perm(a0[ww], a1[ww], hh ? 0x7632 : 0x5410);
           const int seg = (kp >> 1) ^ ((dd >> 2) & 3);
           *reinterpret_cast<uint32_t*>(vt + dd * BK + 4 * seg + 2 * (kp & 1)) = word;
         }
@@ -252,8 +253,12 @@ decode_mfma_kernel(DecodeArgs a) {
     // ---- scores S[h][key] -------------------------------------------------------------
     f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
     if (any_remote) {
-      const int j0c = min(j0, pos), jkc = min(jk, pos);
-      const int dk = (jkc - alias_fast(jkc, a.gdiv)) - (j0c - alias_fast(j0c, a.gdiv));
+      const int jkc = min(jk, pos);
+      const int n0 = j0 - alias_fast(j0, gdiv);
+      const int dk = (jkc - alias_fast(jkc, gdiv)) - n0;
+      // R(n0) of the block: lane = pair (the wave's previous reads of the row are
+      // complete: LDS operations of a wave execute in order)
+      row[lane] = angle_cs(n0, invf);
       const float2* drow = &s_dt[dk][8 * kq];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -261,7 +266,7 @@ decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           // R(n0 + d): compose the block row with the offset row
-          const float4 c0 = cur.t[4 * s + e2];
+          const float4 c0 = *reinterpret_cast<const float4*>(row + 32 * s + 8 * kq + 2 * e2);
           const float4 cd = *reinterpret_cast<const float4*>(drow + 32 * s + 2 * e2);
           const float4 cs = make_float4(c0.x * cd.x - c0.y * cd.y, c0.y * cd.x + c0.x * cd.y,
                                         c0.z * cd.z - c0.w * cd.w, c0.w * cd.z + c0.z * cd.w);
@@ -342,13 +347,13 @@ decode_mfma_kernel(DecodeArgs a) {
     }
   };
   Blk buf0, buf1;
-  if (nblk > 0) load_blk(0, buf0);
-  int b = 0;
-  for (; b + 1 < nblk; b += 2) {
-    block(b, buf0, buf1);
-    block(b + 1, buf1, buf0);
+  if (cnt > 0) load_blk(0, buf0);
+  int i = 0;
+  for (; i + 1 < cnt; i += 2) {
+    block(i, buf0, buf1);
+    block(i + 1, buf1, buf0);
   }
-  if (b < nblk) block(b, buf0, buf1);
+  if (i < cnt) block(i, buf0, buf1);
 
   // ---- merge the four waves (splits) of this workgroup, write one partial per head -----
   float lt[4];
@@ -359,8 +364,8 @@ decode_mfma_kernel(DecodeArgs a) {
   if (l16 == 0)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s_ml[wave][4 * kq + r][0] = nblk > 0 ? m_run[r] : -INFINITY;
-      s_ml[wave][4 * kq + r][1] = nblk > 0 ? lt[r] : 0.f;
+      s_ml[wave][4 * kq + r][0] = cnt > 0 ? m_run[r] : -INFINITY;
+      s_ml[wave][4 * kq + r][1] = cnt > 0 ? lt[r] : 0.f;
     }
   if (l16 < REP) {  // O^T column l16 = head l16: rows 16db + 4kq + r
 #pragma unroll
@@ -369,24 +374,24 @@ decode_mfma_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) s_acc[wave][l16][16 * db + 4 * kq + r] = oacc[db][r];
   }
   __syncthreads();
-  const int wg_split = wsplit / NWD;
-  const int nwg_all = a.nsplit / NWD;
+  const int nwg = a.nwg;
+  const size_t head0 = (size_t)b * a.Hq + (size_t)g * REP;  // first query head of the group
   for (int e = threadIdx.x; e < REP * D; e += 256) {
     const int h = e / D, d = e - h * D;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NWD; ++w) mx = fmaxf(mx, s_ml[w][h][0]);
+    for (int ww = 0; ww < NWD; ++ww) mx = fmaxf(mx, s_ml[ww][h][0]);
     float o = 0.f, l = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < NWD; ++w) {
-        const float ms = s_ml[w][h][0];
+      for (int ww = 0; ww < NWD; ++ww) {
+        const float ms = s_ml[ww][h][0];
         const float wt = ms == -INFINITY ? 0.f : fast_exp2(ms - mx);
-        o += wt * s_acc[w][h][d];
-        l += wt * s_ml[w][h][1];
+        o += wt * s_acc[ww][h][d];
+        l += wt * s_ml[ww][h][1];
       }
     }
-    float* dst = a.part + ((size_t)(g * REP + h) * nwg_all + wg_split) * (D + 2);
+    float* dst = a.part + ((head0 + h) * nwg + wgi) * (D + 2);
     dst[d] = o;
     if (d == 0) {
       dst[D] = mx;
@@ -395,8 +400,65 @@ decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int rep, hipStream_t stream) {
-  const dim3 grid(a.nsplit / dm::NWD * a.Hkv);
+// Merge the partials of each (sequence, query head): O = sum_s w_s acc_s / sum_s w_s l_s
+// with w_s = 2^(m_s - max m), LSE = ln 2 (max m + log2 sum_s w_s l_s).  One workgroup per
+// (sequence, query head, 32 channels); every load is issued up front (one memory round
+// trip), then the maxima, weights and weighted sums are reduced in registers and LDS.
+__global__ void __launch_bounds__(256) decode_mfma_combine_kernel(DecodeBatchArgs a) {
+  constexpr int D = dm::D;
+  constexpr int KP = kDecodeMaxParts / 8;  // partials per lane group of 32
+  __shared__ float s_w[kDecodeMaxParts];
+  __shared__ float s_red[8][33];
+  const int tid = threadIdx.x, grp = tid >> 5, c = tid & 31;
+  const int d0 = 32 * blockIdx.y;
+  const int nwg = a.nwg;
+  const size_t head = (size_t)a.b_base * a.Hq + blockIdx.x;
+  const float* base = a.part + head * nwg * (D + 2);
+  float mv = -INFINITY, lv = 0.f;
+  if (tid < nwg) {
+    mv = base[(size_t)tid * (D + 2) + D];
+    lv = base[(size_t)tid * (D + 2) + D + 1];
+  }
+  float acc[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int s = grp + 8 * k;
+    acc[k] = s < nwg ? base[(size_t)s * (D + 2) + d0 + c] : 0.f;
+  }
+  // max over the partials (64-lane waves, then the four waves)
+  float mx = mv;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) s_red[tid >> 6][32] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0][32], s_red[1][32]), fmaxf(s_red[2][32], s_red[3][32]));
+  const float wt = mv == -INFINITY ? 0.f : exp2f(mv - mx);
+  if (tid < nwg) s_w[tid] = wt;
+  float ls = wt * lv;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
+  __syncthreads();  // s_w complete, s_red[.][32] consumed
+  if ((tid & 63) == 0) s_red[tid >> 6][32] = ls;
+  float o = 0.f;
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int s = grp + 8 * k;
+    if (s < nwg) o += s_w[s] * acc[k];
+  }
+  s_red[grp][c] = o;
+  __syncthreads();
+  if (tid < 32) {
+    const float l = s_red[0][32] + s_red[1][32] + s_red[2][32] + s_red[3][32];
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v += s_red[q][tid];
+    ((uint16_t*)a.o)[head * D + d0 + tid] = (uint16_t)f32_to_bf16_bits(v / l);
+    if (a.lse && blockIdx.y == 0 && tid == 0) a.lse[head] = (mx + log2f(l)) * 0.69314718055994530942f;
+  }
+}
+
+hipError_t launch_decode_mfma(const DecodeBatchArgs& a, int rep, hipStream_t stream) {
+  const dim3 grid(a.nseq * a.nwg * a.Hkv);
   switch (rep) {
     case 1: hipLaunchKernelGGL(decode_mfma_kernel<1>, grid, dim3(256), 0, stream, a); break;
     case 2: hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(256), 0, stream, a); break;
@@ -404,6 +466,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int rep, hipStream_t stream) 
     case 8: hipLaunchKernelGGL(decode_mfma_kernel<8>, grid, dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_mfma_combine_kernel, dim3(a.nseq * a.Hq, dm::D / 32), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -112,15 +112,19 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
  *   from the current length pos + 1 (so it grows as generation crosses multiples of
  *   w_pretrained, without touching the cache: section 2, on-the-fly correction
  *   rotation applied to the active query and the stored keys).  Scores as in
- *   bifocal_prefill with i = pos.  Keys are rotated in float32 registers; dot
- *   products and the softmax run in float32.
+ *   bifocal_prefill with i = pos.  Keys are rotated in float32 registers; the softmax
+ *   runs in float32.
  *   q      (device) [Hq, D] standard RoPE at pos.
  *   Kcache (device) [S, Hkv, D] standard RoPE at absolute positions, S >= pos + 1.
  *   Vcache (device) [S, Hkv, D].
  *   o      (device) [Hq, D] output, dtype dt.   lse (device) [Hq] float32, or NULL.
  *   dt: BF_BF16 or BF_F32 for q, caches and o.  D in {64, 128}; Hq/Hkv in {1, 2, 4, 8}.
+ *     bf16 with D = 128 runs on the matrix cores: remote scores use fp16 hi/lo operands
+ *     of the rotated fp32 keys and query (error well below bf16 rounding), local scores
+ *     the stored bf16 operands, and the correction angles are evaluated in the kernel
+ *     (the workspace table is not read).  Other cases run on the vector units in fp32.
  *   ws, ws_bytes: workspace (device) of at least
- *     bifocal_workspace_bytes(BF_OP_DECODE, pos + 1, 0, 0, Hq, Hkv, D).
+ *     bifocal_workspace_bytes(BF_OP_DECODE, pos + 1, 0, 1, Hq, Hkv, D).
  *   Errors: BF_EINVAL (null pointer, pos < 0, w0 < 1, ...), BF_EUNSUPPORTED, BF_EWORKSPACE.
  */
 bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, void* o,
@@ -129,11 +133,37 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
                          void* ws, size_t ws_bytes, bf_stream stream);
 
 /*
+ * bifocal_decode_batch -- one generation step for each of B sequences of different
+ * lengths (ragged batch decode).
+ *   Sequence b's query sits at position pos[b] and attends to entries 0 .. pos[b] of its
+ *   own cache; its G_b = max(1, ceil((pos[b] + 1) / w_pretrained)) is taken per sequence
+ *   (section 1 with the sequence's current length), so sequences on either side of a
+ *   multiple of w_pretrained use different groupings in the same call.  Each sequence
+ *   is computed exactly as bifocal_decode would compute it alone.
+ *   q      (device) [B, Hq, D] standard RoPE at pos[b].
+ *   Kcache (device) [B, S, Hkv, D] standard RoPE at absolute positions (S rows per
+ *          sequence; rows past pos[b] are not read).
+ *   Vcache (device) [B, S, Hkv, D].
+ *   o      (device) [B, Hq, D] output.   lse (device) [B, Hq] float32, or NULL.
+ *   pos    (host) [B], 0 <= pos[b] < S.
+ *   dt, D, Hq/Hkv as for bifocal_decode.  B = 0 is a no-op.
+ *   ws, ws_bytes: workspace (device) of at least
+ *     bifocal_workspace_bytes(BF_OP_DECODE, max_b pos[b] + 1, 0, B, Hq, Hkv, D).
+ *   Errors: BF_EINVAL (null pointer, B < 0, S < 1, pos[b] outside [0, S), ...),
+ *           BF_EUNSUPPORTED, BF_EWORKSPACE.
+ */
+bf_status bifocal_decode_batch(const void* q, const void* Kcache, const void* Vcache, void* o,
+                               float* lse, const int32_t* pos, int32_t B, int32_t S, int32_t Hq,
+                               int32_t Hkv, int32_t D, int32_t w0, int32_t w_pretrained,
+                               double theta, float softmax_scale, bf_dtype dt, void* ws,
+                               size_t ws_bytes, bf_stream stream);
+
+/*
  * bifocal_workspace_bytes -- workspace size for an operation.
- *   max_len: the longest sequence a prefill will see, or pos + 1 for decode.
- *   total_tokens, num_seqs: prefill only, the largest T and B of the calls that will
- *     use the workspace (max_len <= total_tokens <= num_seqs * max_len); ignored for
- *     decode.
+ *   max_len: the longest sequence a prefill will see, or the largest pos + 1 for decode.
+ *   total_tokens, num_seqs: prefill: the largest T and B of the calls that will use the
+ *     workspace (max_len <= total_tokens <= num_seqs * max_len).  Decode: num_seqs is the
+ *     largest batch B (0 counts as 1), total_tokens is ignored.
  *   Returns 0 for invalid arguments.
  */
 size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int64_t total_tokens,

@@ -124,6 +124,45 @@ def test_decode_rejects_bad_arguments_before_launch(lib):
     assert _decode(lib, ws_bytes=1 << 12) == BF_EWORKSPACE
 
 
+def _decode_batch(lib, **kw):
+    a = dict(q=16, K=16, V=16, o=16, lse=0, pos=[100, 7, 300], B=None, S=512, Hq=4, Hkv=1,
+             D=128, w0=4, w_pre=16, theta=1e4, scale=0.0, dt=1, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    pos = a["pos"]
+    B = len(pos) if a["B"] is None else a["B"]
+    ptr = None
+    if pos is not None:
+        arr = (ctypes.c_int32 * max(len(pos), 1))(*pos)
+        ptr = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.bifocal_decode_batch(a["q"], a["K"], a["V"], a["o"], a["lse"], ptr, B, a["S"],
+                                    a["Hq"], a["Hkv"], a["D"], a["w0"], a["w_pre"], a["theta"],
+                                    a["scale"], a["dt"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_batch_rejects_bad_arguments_before_launch(lib):
+    assert _decode_batch(lib, pos=[100, -1]) == BF_EINVAL
+    assert _decode_batch(lib, pos=[100, 512]) == BF_EINVAL      # pos >= S
+    assert _decode_batch(lib, pos=None, B=2) == BF_EINVAL
+    assert _decode_batch(lib, B=-1) == BF_EINVAL
+    assert _decode_batch(lib, S=0) == BF_EINVAL
+    assert _decode_batch(lib, q=0) == BF_EINVAL
+    assert _decode_batch(lib, w0=0) == BF_EINVAL
+    assert _decode_batch(lib, Hq=12, Hkv=4) == BF_EUNSUPPORTED
+    assert _decode_batch(lib, D=96) == BF_EUNSUPPORTED
+    assert _decode_batch(lib, V=24) == BF_EINVAL                # misaligned
+    assert _decode_batch(lib, ws=0) == BF_EWORKSPACE
+    assert _decode_batch(lib, ws_bytes=1 << 12) == BF_EWORKSPACE
+    assert _decode_batch(lib, pos=[], q=0, K=0, V=0, o=0) == BF_OK   # empty batch
+
+
+def test_decode_workspace_grows_with_batch(lib):
+    one = lib.bifocal_workspace_bytes(2, 4096, 0, 1, 32, 8, 128)
+    assert lib.bifocal_workspace_bytes(2, 4096, 0, 0, 32, 8, 128) == one
+    many = lib.bifocal_workspace_bytes(2, 4096, 0, 16, 32, 8, 128)
+    assert many >= 16 * 32 * 128 * 130 * 4 > one
+    assert lib.bifocal_workspace_bytes(2, 4096, 0, -1, 32, 8, 128) == 0
+
+
 def test_rope_apply_rejects_bad_arguments(lib):
     f = lib.rope_apply
     assert f(16, None, 0, 10, 2, 7, 1e4, 1, 1, None) == BF_EINVAL     # odd D

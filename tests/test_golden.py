@@ -36,3 +36,6 @@ def test_known_values():
     assert [s["G"] for s in f["qwen3_8b_ragged"]["sequences"]] == [4, 2]
     assert f["tiny_f32"]["sequences"][0]["G"] == 4
     assert f["qwen3_1p7b_32k_g1"]["sequences"][0]["G"] == 1
+    # the boundary run ends past L = 4 * w_pretrained: G = 5
+    assert f["qwen3_8b_decode_boundary"]["sequences"][0]["G"] == 5
+    assert f["qwen3_8b_decode_128k"]["sequences"][0]["G"] == 4

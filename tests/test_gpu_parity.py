@@ -224,3 +224,98 @@ def test_decode_equals_prefill_last_row(bf):
         e = errors(host(o), Og[pos], lse.cpu().numpy(), Lg[:, pos])
         say(f"  pos={pos} decode vs prefill row: {e}")
         assert within(e, BF16_TOL)
+
+
+# ---------------------------------------------------------------------------
+# batched (ragged) decode and the length boundary
+# ---------------------------------------------------------------------------
+
+def _batch_caches(w, B, S):
+    """B independently seeded caches [B,S,Hkv,D] and raw queries [B,Hq,D]."""
+    qs, Ks, Vs = [], [], []
+    for b in range(B):
+        q_raw, Kc, Vc = decode_inputs(dataclasses.replace(w, seed=w.seed + 10 * b), S=S)
+        qs.append(q_raw[0])
+        Ks.append(Kc)
+        Vs.append(Vc)
+    return np.stack(qs), np.stack(Ks), np.stack(Vs)
+
+
+@pytest.mark.parametrize("dt,D,Hq,Hkv", [("bf16", 128, 32, 8), ("bf16", 128, 8, 1),
+                                         ("f32", 128, 4, 4), ("bf16", 64, 8, 2)])
+def test_decode_batch_matches_oracle(bf, dt, D, Hq, Hkv):
+    # ragged positions: G = 1, 1, 2, 3, 3 at w_pretrained 1000; window edges and a
+    # one-key cache
+    w = W.Workload("decb", "decode", dt, Hq=Hq, Hkv=Hkv, D=D, w0=100, w_pretrained=1000,
+                   theta=1e6, cache_len=3000, decode_steps=1, outliers=4, seed=77)
+    positions = [0, 999, 1000, 2001, 2999, 100, 57]
+    B, S = len(positions), 3000
+    say("decode batch", w, positions)
+    q_raw, Kc, Vc = _batch_caches(w, B, S)
+    q = np.stack([std_query(q_raw[b], positions[b], w.theta, dt) for b in range(B)])
+    o, lse = bf.bifocal_decode_batch(dev(q, dt), dev(Kc, dt), dev(Vc, dt), positions, w.w0,
+                                     w.w_pretrained, w.theta)
+    torch.cuda.synchronize()
+    og, lg = host(o), lse.cpu().numpy()
+    tol = BF16_TOL if dt == "bf16" else F32_TOL
+    for b, pos in enumerate(positions):
+        Or, Lr = bifocal_decode_ref(q[b], Kc[b], Vc[b], pos, w.w0, w.w_pretrained, w.theta)
+        e = errors(og[b], Or, lg[b], Lr)
+        say(f"  seq {b} pos={pos} G={group_size(pos + 1, w.w_pretrained)} {e}")
+        assert within(e, tol), (b, pos, e)
+
+
+def test_decode_batch_sequences_do_not_interact(bf):
+    # a sequence's result does not depend on the other members of its batch
+    w = W.Workload("decb2", "decode", "bf16", Hq=16, Hkv=4, D=128, w0=64, w_pretrained=512,
+                   theta=1e6, cache_len=2048, decode_steps=1, seed=91)
+    positions = [2047, 600, 1500]
+    q_raw, Kc, Vc = _batch_caches(w, 3, 2048)
+    q = np.stack([std_query(q_raw[b], positions[b], w.theta, "bf16") for b in range(3)])
+    qd, Kd, Vd = dev(q, "bf16"), dev(Kc, "bf16"), dev(Vc, "bf16")
+    o_all, l_all = bf.bifocal_decode_batch(qd, Kd, Vd, positions, w.w0, w.w_pretrained, w.theta)
+    o_one, l_one = bf.bifocal_decode_batch(qd[1:2].contiguous(), Kd[1:2].contiguous(),
+                                           Vd[1:2].contiguous(), positions[1:2], w.w0,
+                                           w.w_pretrained, w.theta)
+    torch.cuda.synchronize()
+    Or, Lr = bifocal_decode_ref(q[1], Kc[1], Vc[1], positions[1], w.w0, w.w_pretrained, w.theta)
+    for o, l in ((o_all[1], l_all[1]), (o_one[0], l_one[0])):
+        e = errors(host(o), Or, l.cpu().numpy(), Lr)
+        say(f"  seq 1 {e}")
+        assert within(e, BF16_TOL), e
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_across_length_boundary(bf, dt):
+    # w_pretrained 256: G is 4 up to L = 1024 and 5 from L = 1025 on; the cache is the
+    # same bytes throughout (standard RoPE at absolute positions), only G changes
+    w = W.Workload("bound", "decode", dt, Hq=8, Hkv=2, D=128, w0=48, w_pretrained=256,
+                   theta=1e4, cache_len=1100, decode_steps=8, outliers=4, seed=123)
+    q_raw, Kc, Vc = decode_inputs(w)
+    Kd, Vd = dev(Kc, dt), dev(Vc, dt)
+    ws = bf.Workspace.for_op(bf.OP_DECODE, 1100, w.Hq, w.Hkv, w.D, num_seqs=4)
+    tol = BF16_TOL if dt == "bf16" else F32_TOL
+    positions = [1021, 1022, 1023, 1024, 1025, 1026, 1099]
+    assert [group_size(p + 1, 256) for p in positions] == [4, 4, 4, 5, 5, 5, 5]
+    qs = [std_query(q_raw[i % 8], p, w.theta, dt) for i, p in enumerate(positions)]
+    refs = [bifocal_decode_ref(q, Kc, Vc, p, w.w0, w.w_pretrained, w.theta)
+            for q, p in zip(qs, positions)]
+    for q, p, (Or, Lr) in zip(qs, positions, refs):  # one step at a time
+        o, lse = bf.bifocal_decode(dev(q, dt), Kd, Vd, p, w.w0, w.w_pretrained, w.theta,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        e = errors(host(o), Or, lse.cpu().numpy(), Lr)
+        say(f"  pos={p} G={group_size(p + 1, 256)} {e}")
+        assert within(e, tol), (p, e)
+    # both sides of the boundary in one batched call over copies of the same cache
+    sel = [2, 3, 4, 0]
+    qb = np.stack([qs[i] for i in sel])
+    Kb = Kd.unsqueeze(0).expand(len(sel), -1, -1, -1).contiguous()
+    Vb = Vd.unsqueeze(0).expand(len(sel), -1, -1, -1).contiguous()
+    o, lse = bf.bifocal_decode_batch(dev(qb, dt), Kb, Vb, [positions[i] for i in sel], w.w0,
+                                     w.w_pretrained, w.theta, workspace=ws)
+    torch.cuda.synchronize()
+    for k, i in enumerate(sel):
+        e = errors(host(o[k]), refs[i][0], lse[k].cpu().numpy(), refs[i][1])
+        say(f"  batch member {k} pos={positions[i]} {e}")
+        assert within(e, tol), (positions[i], e)

@@ -89,3 +89,43 @@ def test_qwen3_8b_decode_128k(bf):
                 f" {err}")
             assert within(err, BF16_TOL), err
     torch.cuda.synchronize()
+
+
+def test_qwen3_8b_decode_across_boundary(bf):
+    # 258 consecutive steps from position 131071 (G = 4) to 131328 (G = 5 from 131072 on),
+    # over one cache that is never rewritten; then both sides of the boundary in one
+    # batched call
+    w = W.get("qwen3_8b_decode_boundary")
+    say("decode boundary: building the cache on the CPU")
+    q_raw, Kc, Vc = decode_inputs(w)
+    Kd, Vd = dev(Kc), dev(Vc)
+    ws = bf.Workspace.for_op(bf.OP_DECODE, w.cache_len, w.Hq, w.Hkv, w.D, num_seqs=2)
+    positions = w.decode_positions()
+    assert int(positions[0]) == 131071 and int(positions[-1]) == 131328
+    checked = {0, 1, 2, len(positions) - 1}
+    qs = {}
+    for step, pos in enumerate(positions):
+        q = std_query(q_raw[step], int(pos), w.theta, "bf16")
+        o, lse = bf.bifocal_decode(dev(q), Kd, Vd, int(pos), w.w0, w.w_pretrained, w.theta,
+                                   workspace=ws)
+        if step in checked:
+            qs[step] = q
+            torch.cuda.synchronize()
+            Or, Lr = bifocal_decode_ref(q, Kc, Vc, int(pos), w.w0, w.w_pretrained, w.theta)
+            err = errors(o.float().cpu().numpy(), Or, lse.cpu().numpy(), Lr)
+            say(f"decode step {step} pos={int(pos)} G={group_size(int(pos) + 1, w.w_pretrained)}"
+                f" {err}")
+            assert within(err, BF16_TOL), err
+    torch.cuda.synchronize()
+    Kb = Kd.unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+    Vb = Vd.unsqueeze(0).expand(2, -1, -1, -1).contiguous()
+    pb = [int(positions[0]), int(positions[1])]
+    qb = np.stack([qs[0], qs[1]])
+    o, lse = bf.bifocal_decode_batch(dev(qb), Kb, Vb, pb, w.w0, w.w_pretrained, w.theta,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    for k, pos in enumerate(pb):
+        Or, Lr = bifocal_decode_ref(qb[k], Kc, Vc, pos, w.w0, w.w_pretrained, w.theta)
+        err = errors(o[k].float().cpu().numpy(), Or, lse[k].cpu().numpy(), Lr)
+        say(f"batched pos={pos} G={group_size(pos + 1, w.w_pretrained)} {err}")
+        assert within(err, BF16_TOL), err

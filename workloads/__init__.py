@@ -73,6 +73,11 @@ WORKLOADS = {
     "qwen3_8b_decode_128k": Workload("qwen3_8b_decode_128k", "decode", "bf16", Hq=32, Hkv=8,
                                      D=128, w0=4096, w_pretrained=32768, theta=1e6,
                                      cache_len=131072, decode_steps=256, seed=4000),
+    # The same decode layer generating across the length boundary L = 4 * 32768 + 1, where G
+    # goes from 4 to 5 while the cache stays as stored (positions 131071 .. 131328).
+    "qwen3_8b_decode_boundary": Workload("qwen3_8b_decode_boundary", "decode", "bf16", Hq=32,
+                                         Hkv=8, D=128, w0=4096, w_pretrained=32768, theta=1e6,
+                                         cache_len=131329, decode_steps=258, seed=4100),
     # Qwen3-8B ragged prefill: two sequences with their own G (4 and 2), ragged tails.
     "qwen3_8b_ragged": Workload("qwen3_8b_ragged", "prefill", "bf16", Hq=32, Hkv=8, D=128,
                                 w0=8192, w_pretrained=32768, theta=1e6,
