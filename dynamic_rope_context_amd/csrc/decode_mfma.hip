@@ -141,6 +141,40 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   const uint32_t rs = (uint32_t)a.Hkv * D;  // elements between consecutive cache rows
   const uint16_t* kg = (const uint16_t*)a.K + (size_t)b * a.seq_stride + (size_t)g * D;
   const uint16_t* vg = (const uint16_t*)a.V + (size_t)b * a.seq_stride + (size_t)g * D;
+  // Block loads, one block ahead: K (key l16, channels 32s + 8kq + e) and V (keys 2kp,
+  // 2kp+1 of channel group cg = 16 channels).  Keys past pos are clamped to pos (their
+  // scores are masked).
+  const int kp = lane & 7, cg = lane >> 3;
+  struct Blk {
+    uint4 k[4];
+    uint4 v[2][2];
+  };
+  auto load_blk = [&](int i, Blk& x) __attribute__((always_inline)) {
+    const int j0 = (w + i * nsplit) * BK;
+    const int jk = min(j0 + l16, pos);
+    const uint16_t* kr = kg + (uint32_t)jk * rs + 8 * kq;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int jv = min(j0 + 2 * kp + k2, pos);
+      const uint16_t* vr = vg + (uint32_t)jv * rs + 16 * cg;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) x.v[k2][c] = *reinterpret_cast<const uint4*>(vr + 8 * c);
+    }
+  };
+
+  // The query and the first block's loads go out before the set-up work below (angles,
+  // query rotation); the block's loads stay in flight across its barrier.
+  uint4 raw[4];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)b * a.Hq + g * REP + min(l16, REP - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * kq);
+  }
+  Blk buf0, buf1;
+  load_blk(0, buf0);  // unconditional (clamped to pos): keeps the wait counts static
+
   const double invf = inv_freq64(a.theta, lane, D);  // lane = RoPE pair
   float2* row = s_row[wave];
 
@@ -153,13 +187,9 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   // lane (head l16, group kq) holds channels 32s + 8kq + e, s = 0..3
   u32x4 qh[4], ql[4];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)b * a.Hq + g * REP + min(l16, REP - 1)) * D;
-    uint4 raw[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      raw[s] = *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * kq);
+    for (int s = 0; s < 4; ++s)
       if (l16 >= REP) raw[s] = make_uint4(0u, 0u, 0u, 0u);
-    }
     uint16_t* sq = s_q[wave];
     if (l16 < REP)
 #pragma unroll
@@ -185,7 +215,9 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     }
   }
   const uint16_t* sq_row = s_q[wave] + (l16 < REP ? l16 : 8) * D + 8 * kq;
-  __syncthreads();  // offset rows complete
+  // offset rows complete (LDS only: a plain __syncthreads would also wait for the
+  // block loads in flight)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   f32x4 oacc[8];  // O^T blocks [16 channels][16 head columns]
 #pragma unroll
@@ -196,29 +228,6 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     m_run[r] = -1e30f;
     l_run[r] = 0.f;
   }
-
-  // Block loads, one block ahead: K (key l16, channels 32s + 8kq + e) and V (keys 2kp,
-  // 2kp+1 of channel group cg = 16 channels).  Keys past pos are clamped to pos (their
-  // scores are masked).
-  const int kp = lane & 7, cg = lane >> 3;
-  struct Blk {
-    uint4 k[4];
-    uint4 v[2][2];
-  };
-  auto load_blk = [&](int i, Blk& x) __attribute__((always_inline)) {
-    const int j0 = (w + i * nsplit) * BK;
-    const int jk = min(j0 + l16, pos);
-    const uint16_t* kr = kg + (uint32_t)jk * rs + 8 * kq;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int jv = min(j0 + 2 * kp + k2, pos);
-      const uint16_t* vr = vg + (uint32_t)jv * rs + 16 * cg;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) x.v[k2][c] = *reinterpret_cast<const uint4*>(vr + 8 * c);
-    }
-  };
 
   uint16_t* vt = s_vt[wave];
   uint16_t* pt = s_p[wave];
@@ -346,8 +355,6 @@ decode_mfma_kernel(DecodeBatchArgs a) {
       oacc[db] = mfma16k16_bf16(va, pb, oacc[db]);
     }
   };
-  Blk buf0, buf1;
-  if (cnt > 0) load_blk(0, buf0);
   int i = 0;
   for (; i + 1 < cnt; i += 2) {
     block(i, buf0, buf1);
