@@ -12,6 +12,9 @@ Prints one JSON line on stdout; progress goes to stderr.
              set over the local window: F = 4*D*Hq*sum_i(i+1) + 2*D*Hq*sum_i min(i+1, w0)
   roofline   the prefill kernel against the dense bf16 MFMA peak (2500 TFLOP/s)
   decode     KV GB/s = bytes of K and V read per step / step time, against 8000 GB/s
+  vanilla    the same calls with w0 >= L (every pair local, i.e. causal attention with
+             standard RoPE, no remote branch): prefill and decode times and the bifocal /
+             vanilla ratios, the local analogue of the pages' overhead figures
   cpu_baseline  the CPU oracle timed on sampled query rows, extrapolated by pair count
   traffic    HBM bytes per launch of the timed kernel from rocprofv3 FETCH_SIZE and
              WRITE_SIZE counters (profiles/hbm_traffic.json), scaled by what the same
@@ -99,8 +102,12 @@ def prefill_flops(seqlens, w0, Hq, D):
     return 4 * D * Hq * pc + 2 * D * Hq * pw, 4 * D * Hq * pc
 
 
-def bench_prefill(bf, torch, W, steps, warmup):
+def bench_prefill(bf, torch, W, steps, warmup, w0=None):
+    """w0 overrides the window (w0 >= L: vanilla mode, every pair local)."""
     w = W.get("qwen3_4b_128k")
+    if w0 is not None:
+        import dataclasses
+        w = dataclasses.replace(w, w0=w0)
     T = w.total_tokens
     q, k, v = W.raw_inputs_torch(w, "cuda")
     # standard RoPE at absolute positions, built with the library's own rope_apply
@@ -130,8 +137,12 @@ def bench_prefill(bf, torch, W, steps, warmup):
     return w, ms, F, Fc
 
 
-def bench_decode(bf, torch, W, passes, warmup):
+def bench_decode(bf, torch, W, passes, warmup, w0=None):
+    """w0 overrides the window (w0 > pos: vanilla mode, every key local)."""
     w = W.get("qwen3_8b_decode_128k")
+    if w0 is not None:
+        import dataclasses
+        w = dataclasses.replace(w, w0=w0)
     q, k, v = W.raw_inputs_torch(w, "cuda")
     bf.rope_apply(k, w.theta)
     positions = w.decode_positions()
@@ -208,6 +219,8 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="--only copy: bytes copied per launch, MiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vanilla", action="store_true",
+                    help="skip the vanilla-mode (w0 >= L) comparison runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -268,6 +281,29 @@ def main():
                            "dtype": "bf16", "data": "synthetic",
                            "config": {"workload": "qwen3_8b_decode_128k"},
                            "roofline": dec["roofline"]})
+    if not args.no_vanilla and args.only in ("all", "prefill", "decode"):
+        van = {"mode": "same kernels with w0 >= L: every pair local (standard RoPE), "
+                       "remote branch empty"}
+        if args.only in ("all", "prefill"):
+            log("vanilla prefill: qwen3_4b_128k with w0 = L")
+            wv, vms, _, Fc = bench_prefill(bf, torch, W, args.steps, args.warmup,
+                                           w0=W.get("qwen3_4b_128k").total_tokens)
+            van.update({"prefill_ms": round(vms, 4),
+                        "prefill_causal_tflops": round(Fc / (vms * 1e-3) / 1e12, 3),
+                        "prefill_time_ratio": round(result["ms_per_step"] / vms, 4)})
+            log(f"vanilla prefill: {vms:.2f} ms, bifocal/vanilla time "
+                f"{van['prefill_time_ratio']:.3f}")
+        if args.only in ("all", "decode"):
+            log("vanilla decode: qwen3_8b_decode_128k with w0 = cache length")
+            wv, vms_step, _ = bench_decode(bf, torch, W, args.decode_passes, args.decode_warmup,
+                                           w0=W.get("qwen3_8b_decode_128k").cache_len)
+            us_b = (result["decode"]["us_per_step"] if "decode" in result
+                    else result["ms_per_step"] / W.get("qwen3_8b_decode_128k").decode_steps * 1e3)
+            van.update({"decode_us_per_step": round(vms_step * 1e3, 2),
+                        "decode_overhead": round(us_b / (vms_step * 1e3) - 1.0, 4)})
+            log(f"vanilla decode: {vms_step * 1e3:.1f} us/step, bifocal overhead "
+                f"{100 * van['decode_overhead']:.1f}%")
+        result["vanilla"] = van
     if args.only in ("all", "prefill") and not args.no_cpu_baseline:
         log("cpu baseline: oracle on sampled rows")
         result["cpu_baseline"] = cpu_baseline(W, result["flops_per_step"])
