@@ -12,6 +12,9 @@ Prints one JSON line on stdout; progress goes to stderr.
              set over the local window: F = 4*D*Hq*sum_i(i+1) + 2*D*Hq*sum_i min(i+1, w0)
   roofline   the prefill kernel against the dense bf16 MFMA peak (2500 TFLOP/s)
   decode     KV GB/s = bytes of K and V read per step / step time, against 8000 GB/s
+  three_pass the literal inclusion-exclusion form of the same prefill (local/window,
+             remote/causal and remote/window passes merged by their LSEs): time and the
+             ratio to the fused call
   vanilla    the same calls with w0 >= L (every pair local, i.e. causal attention with
              standard RoPE, no remote branch): prefill and decode times and the bifocal /
              vanilla ratios, the local analogue of the pages' overhead figures
@@ -102,8 +105,9 @@ def prefill_flops(seqlens, w0, Hq, D):
     return 4 * D * Hq * pc + 2 * D * Hq * pw, 4 * D * Hq * pc
 
 
-def bench_prefill(bf, torch, W, steps, warmup, w0=None):
-    """w0 overrides the window (w0 >= L: vanilla mode, every pair local)."""
+def bench_prefill(bf, torch, W, steps, warmup, w0=None, three_pass=False):
+    """w0 overrides the window (w0 >= L: vanilla mode, every pair local); three_pass
+    times the literal inclusion-exclusion form (three passes + LSE merge)."""
     w = W.get("qwen3_4b_128k")
     if w0 is not None:
         import dataclasses
@@ -116,10 +120,11 @@ def bench_prefill(bf, torch, W, steps, warmup, w0=None):
     cu = [int(c) for c in w.cu_seqlens]
     out = torch.empty_like(q)
     lse = torch.empty((w.Hq, T), dtype=torch.float32, device="cuda")
-    ws = bf.Workspace.for_op(bf.OP_PREFILL, max(w.seqlens), w.Hq, w.Hkv, w.D,
+    op = bf.OP_PREFILL_IE if three_pass else bf.OP_PREFILL
+    ws = bf.Workspace.for_op(op, max(w.seqlens), w.Hq, w.Hkv, w.D,
                              total_tokens=T, num_seqs=len(w.seqlens))
-    call = lambda: bf.bifocal_prefill(q, k, v, cu, w.w0, w.w_pretrained, w.theta, out=out,
-                                      lse=lse, workspace=ws)
+    fn = bf.bifocal_prefill_ie if three_pass else bf.bifocal_prefill
+    call = lambda: fn(q, k, v, cu, w.w0, w.w_pretrained, w.theta, out=out, lse=lse, workspace=ws)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -221,6 +226,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vanilla", action="store_true",
                     help="skip the vanilla-mode (w0 >= L) comparison runs")
+    ap.add_argument("--no-three-pass", action="store_true",
+                    help="skip the three-pass inclusion-exclusion comparison run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -281,6 +288,12 @@ def main():
                            "dtype": "bf16", "data": "synthetic",
                            "config": {"workload": "qwen3_8b_decode_128k"},
                            "roofline": dec["roofline"]})
+    if not args.no_three_pass and args.only in ("all", "prefill"):
+        log("three-pass prefill: qwen3_4b_128k, passes A, B, C + merge")
+        _, tms, _, _ = bench_prefill(bf, torch, W, args.steps, args.warmup, three_pass=True)
+        result["three_pass"] = {"prefill_ms": round(tms, 4),
+                                "time_ratio_vs_fused": round(tms / result["ms_per_step"], 4)}
+        log(f"three-pass prefill: {tms:.2f} ms, {tms / result['ms_per_step']:.3f}x the fused call")
     if not args.no_vanilla and args.only in ("all", "prefill", "decode"):
         van = {"mode": "same kernels with w0 >= L: every pair local (standard RoPE), "
                        "remote branch empty"}

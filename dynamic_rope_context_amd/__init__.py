@@ -15,15 +15,15 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = [
-    "lib", "lib_path", "rope_apply", "bifocal_prefill", "bifocal_decode", "bifocal_decode_batch",
-    "workspace_bytes",
-    "group_size", "Workspace", "BifocalError", "OP_PREFILL", "OP_DECODE",
+    "lib", "lib_path", "rope_apply", "bifocal_prefill", "bifocal_prefill_ie", "bifocal_decode",
+    "bifocal_decode_batch", "workspace_bytes", "group_size", "Workspace", "BifocalError",
+    "OP_PREFILL", "OP_DECODE", "OP_PREFILL_IE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libbifocal.so")
 
-OP_ROPE, OP_PREFILL, OP_DECODE = 0, 1, 2
+OP_ROPE, OP_PREFILL, OP_DECODE, OP_PREFILL_IE = 0, 1, 2, 3
 _F32, _BF16 = 0, 1
 
 
@@ -43,6 +43,8 @@ def _load():
     lib.bifocal_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64,
                                     f32, i32, vp, sz, vp]
     lib.bifocal_prefill.restype = i32
+    lib.bifocal_prefill_ie.argtypes = lib.bifocal_prefill.argtypes
+    lib.bifocal_prefill_ie.restype = i32
     lib.bifocal_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f32,
                                    i32, vp, sz, vp]
     lib.bifocal_decode.restype = i32
@@ -145,14 +147,8 @@ def rope_apply(x: torch.Tensor, theta: float, pos: Optional[torch.Tensor] = None
     return x
 
 
-def bifocal_prefill(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
-                    cu_seqlens: Sequence[int], w0: int, w_pretrained: int, theta: float,
-                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                    workspace: Optional[Workspace] = None, stream=None
-                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Bifocal causal attention over packed sequences.  Q [T,Hq,D], K/V [T,Hkv,D] carry
-    standard RoPE at local positions.  Returns (O [T,Hq,D], LSE [Hq,T] float32 or None)."""
+def _prefill(fn, op, Q, K, V, cu_seqlens, w0, w_pretrained, theta, softmax_scale, out, lse,
+             want_lse, workspace, stream, what):
     if Q.dim() != 3 or K.dim() != 3 or V.shape != K.shape:
         raise BifocalError("expected Q [T,Hq,D], K and V [T,Hkv,D]")
     T, Hq, D = Q.shape
@@ -168,15 +164,41 @@ def bifocal_prefill(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
         lse = torch.empty((Hq, T), dtype=torch.float32, device=Q.device)
     if workspace is None:
         max_len = max([cu[b + 1] - cu[b] for b in range(B)] + [0])
-        workspace = Workspace.for_op(OP_PREFILL, max(max_len, 1), Hq, Hkv, D, Q.device,
+        workspace = Workspace.for_op(op, max(max_len, 1), Hq, Hkv, D, Q.device,
                                      total_tokens=max(T, max_len, 1), num_seqs=max(B, 1))
-    _check(lib().bifocal_prefill(
+    _check(fn(
         _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
         _dev(lse, "lse") if lse is not None else 0,
         ctypes.cast(cu_arr, ctypes.c_void_p), B, Hq, Hkv, D, int(w0), int(w_pretrained),
         float(theta), float(softmax_scale), _dtype_code(Q), workspace.ptr, workspace.nbytes,
-        _stream(stream)), "bifocal_prefill")
+        _stream(stream)), what)
     return out, lse
+
+
+def bifocal_prefill(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                    cu_seqlens: Sequence[int], w0: int, w_pretrained: int, theta: float,
+                    softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                    workspace: Optional[Workspace] = None, stream=None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Bifocal causal attention over packed sequences.  Q [T,Hq,D], K/V [T,Hkv,D] carry
+    standard RoPE at local positions.  Returns (O [T,Hq,D], LSE [Hq,T] float32 or None)."""
+    return _prefill(lib().bifocal_prefill, OP_PREFILL, Q, K, V, cu_seqlens, w0, w_pretrained,
+                    theta, softmax_scale, out, lse, want_lse, workspace, stream,
+                    "bifocal_prefill")
+
+
+def bifocal_prefill_ie(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                       cu_seqlens: Sequence[int], w0: int, w_pretrained: int, theta: float,
+                       softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                       workspace: Optional[Workspace] = None, stream=None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The same attention computed as three passes (local/window, remote/causal,
+    remote/window) merged by inclusion-exclusion of their LSEs (bf16 only)."""
+    return _prefill(lib().bifocal_prefill_ie, OP_PREFILL_IE, Q, K, V, cu_seqlens, w0,
+                    w_pretrained, theta, softmax_scale, out, lse, want_lse, workspace, stream,
+                    "bifocal_prefill_ie")
 
 
 def bifocal_decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, pos: int,

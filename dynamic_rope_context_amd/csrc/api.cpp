@@ -33,6 +33,9 @@ int prefill_mfma_positions_per_block(int rep);
 
 hipError_t launch_decode(const DecodeArgs& a, int rep, int D, bool bf16, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeBatchArgs& a, int rep, hipStream_t stream);
+hipError_t launch_ie_merge(const float* oa, const float* ob, const float* oc, const float* la,
+                           const float* lb, const float* lc, void* o, float* lse, int T, int Hq,
+                           hipStream_t stream);
 }  // namespace bifocal
 
 using namespace bifocal;
@@ -92,55 +95,12 @@ bf_status ensure_table(void* ws, const WsLayout& lay, int D, double theta, int n
   return BF_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* bifocal_status_string(int32_t s) {
-  switch (s) {
-    case BF_OK: return "ok";
-    case BF_EINVAL: return "invalid argument";
-    case BF_EUNSUPPORTED: return "unsupported configuration";
-    case BF_EWORKSPACE: return "workspace missing or too small";
-    case BF_EHIP: return "HIP launch or runtime error";
-    default: return "unknown status";
-  }
-}
-
-int32_t bifocal_group_size(int64_t L, int32_t w_pretrained) { return group_size(L, w_pretrained); }
-
-size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int64_t total_tokens,
-                               int32_t num_seqs, int32_t Hq, int32_t Hkv, int32_t D) {
-  if (op < 0 || op > 2 || max_len < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || (D != 64 && D != 128))
-    return 0;
-  if (op == BF_OP_ROPE) return 0;
-  if (op == BF_OP_PREFILL && (total_tokens < max_len || num_seqs < 1 ||
-                              total_tokens > (int64_t)num_seqs * max_len))
-    return 0;
-  if (op == BF_OP_DECODE && num_seqs < 0) return 0;
-  return ws_bytes_for(op, max_len, total_tokens, num_seqs, Hq, Hkv, D);
-}
-
-bf_status rope_apply(void* x, const int32_t* pos, int32_t pos0, int32_t T, int32_t H, int32_t D,
-                     double theta, int32_t G, bf_dtype dt, bf_stream stream) {
-  if (T < 0 || H < 1 || D < 2 || (D & 1) || G < 1 || !(theta > 0.0) || !std::isfinite(theta))
-    return BF_EINVAL;
-  if (dt != BF_F32 && dt != BF_BF16) return BF_EINVAL;
-  if (D > 256) return BF_EUNSUPPORTED;
-  if (T == 0) return BF_OK;
-  if (!x) return BF_EINVAL;
-  if (!pos && (pos0 < 0 || (int64_t)pos0 + T - 1 > INT32_MAX)) return BF_EINVAL;
-  if (!aligned(x, dt == BF_BF16 ? 2 : 4) || (pos && !aligned(pos, 4))) return BF_EINVAL;
-  hipError_t e = launch_rope_apply(x, pos, pos0, T, H, D, theta, G, dt == BF_BF16,
-                                   (hipStream_t)stream);
-  return e == hipSuccess ? BF_OK : BF_EHIP;
-}
-
-bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, float* lse,
-                          const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
-                          int32_t D, int32_t w0, int32_t w_pretrained, double theta,
-                          float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
-                          bf_stream stream) {
+// Shared by bifocal_prefill (ie = false) and bifocal_prefill_ie (ie = true: the three
+// inclusion-exclusion passes into fp32 intermediates, then the merge).
+bf_status prefill_impl(const void* Q, const void* K, const void* V, void* O, float* lse,
+                       const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                       int32_t w0, int32_t w_pretrained, double theta, float softmax_scale,
+                       bf_dtype dt, void* ws, size_t ws_bytes, bf_stream stream, bool ie) {
   if (!cu_seqlens || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 1 || w_pretrained < 1 ||
       !(theta > 0.0) || !std::isfinite(theta) || !std::isfinite(softmax_scale))
     return BF_EINVAL;
@@ -160,6 +120,7 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
   const int rep = Hq / Hkv;
   if (dt == BF_BF16 && (D != 128 || (rep != 1 && rep != 2 && rep != 4 && rep != 8)))
     return BF_EUNSUPPORTED;
+  if (ie && dt != BF_BF16) return BF_EUNSUPPORTED;
   if (T == 0) return BF_OK;
   if (!Q || !K || !V || !O) return BF_EINVAL;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
@@ -172,8 +133,9 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
     for (int b = 0; b < B; ++b)
       tiles += (cu_seqlens[b + 1] - cu_seqlens[b] + kKeyTileKeys - 1) / kKeyTileKeys;
   if (tiles > INT32_MAX) return BF_EUNSUPPORTED;
+  const size_t rec_bytes = dt == BF_BF16 ? records_bytes(Hkv, tiles) : 0;
   const WsLayout lay =
-      ws_layout(BF_OP_PREFILL, Hq, Hkv, D, ws_bytes, dt == BF_BF16 ? records_bytes(Hkv, tiles) : 0);
+      ws_layout(BF_OP_PREFILL, Hq, Hkv, D, ws_bytes, rec_bytes + (ie ? ie_bytes(T, Hq, D) : 0));
   if (lay.scratch_off == 0 || lay.n_cap < max_len) return BF_EWORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
@@ -204,6 +166,19 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
   a.D = D;
   a.w0 = w0;
   a.scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  // inclusion-exclusion intermediates (pass A: local/window, B: remote/causal,
+  // C: remote/window), after the records
+  float* ie_o[3] = {nullptr, nullptr, nullptr};
+  float* ie_l[3] = {nullptr, nullptr, nullptr};
+  if (ie) {
+    char* p = wsb + lay.rec_off + rec_bytes;
+    for (int x = 0; x < 3; ++x) {
+      ie_o[x] = reinterpret_cast<float*>(p);
+      p += align_up((size_t)T * Hq * D * sizeof(float), 256);
+      ie_l[x] = reinterpret_cast<float*>(p);
+      p += align_up((size_t)Hq * T * sizeof(float), 256);
+    }
+  }
   const int rows = dt == BF_BF16 ? prefill_mfma_positions_per_block(rep)
                                  : prefill_f32_rows_per_block();
   int32_t tile_base = 0;
@@ -228,11 +203,88 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
     if (n == 0) continue;
     a.nseq = n;
     a.max_qblocks = maxq;
-    hipError_t e = dt == BF_BF16 ? launch_prefill_mfma(a, chunk_tiles, st)
-                                 : launch_prefill_f32(a, st);
-    if (e != hipSuccess) return BF_EHIP;
+    if (!ie) {
+      hipError_t e = dt == BF_BF16 ? launch_prefill_mfma(a, chunk_tiles, st)
+                                   : launch_prefill_f32(a, st);
+      if (e != hipSuccess) return BF_EHIP;
+      continue;
+    }
+    static const int kModes[3] = {3, 1, 2};  // passes A, B, C
+    a.out_f32 = 1;
+    for (int x = 0; x < 3; ++x) {
+      a.mode = kModes[x];
+      a.O = ie_o[x];
+      a.lse = ie_l[x];
+      // the key records are written once per chunk, by the first pass
+      if (launch_prefill_mfma(a, x == 0 ? chunk_tiles : 0, st) != hipSuccess) return BF_EHIP;
+    }
   }
+  if (ie && launch_ie_merge(ie_o[0], ie_o[1], ie_o[2], ie_l[0], ie_l[1], ie_l[2], O, lse, T, Hq,
+                            st) != hipSuccess)
+    return BF_EHIP;
   return BF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bifocal_status_string(int32_t s) {
+  switch (s) {
+    case BF_OK: return "ok";
+    case BF_EINVAL: return "invalid argument";
+    case BF_EUNSUPPORTED: return "unsupported configuration";
+    case BF_EWORKSPACE: return "workspace missing or too small";
+    case BF_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t bifocal_group_size(int64_t L, int32_t w_pretrained) { return group_size(L, w_pretrained); }
+
+size_t bifocal_workspace_bytes(int32_t op, int32_t max_len, int64_t total_tokens,
+                               int32_t num_seqs, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (op < 0 || op > 3 || max_len < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || (D != 64 && D != 128))
+    return 0;
+  if (op == BF_OP_ROPE) return 0;
+  if ((op == BF_OP_PREFILL || op == BF_OP_PREFILL_IE) && (total_tokens < max_len || num_seqs < 1 ||
+                              total_tokens > (int64_t)num_seqs * max_len))
+    return 0;
+  if (op == BF_OP_DECODE && num_seqs < 0) return 0;
+  return ws_bytes_for(op, max_len, total_tokens, num_seqs, Hq, Hkv, D);
+}
+
+bf_status rope_apply(void* x, const int32_t* pos, int32_t pos0, int32_t T, int32_t H, int32_t D,
+                     double theta, int32_t G, bf_dtype dt, bf_stream stream) {
+  if (T < 0 || H < 1 || D < 2 || (D & 1) || G < 1 || !(theta > 0.0) || !std::isfinite(theta))
+    return BF_EINVAL;
+  if (dt != BF_F32 && dt != BF_BF16) return BF_EINVAL;
+  if (D > 256) return BF_EUNSUPPORTED;
+  if (T == 0) return BF_OK;
+  if (!x) return BF_EINVAL;
+  if (!pos && (pos0 < 0 || (int64_t)pos0 + T - 1 > INT32_MAX)) return BF_EINVAL;
+  if (!aligned(x, dt == BF_BF16 ? 2 : 4) || (pos && !aligned(pos, 4))) return BF_EINVAL;
+  hipError_t e = launch_rope_apply(x, pos, pos0, T, H, D, theta, G, dt == BF_BF16,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? BF_OK : BF_EHIP;
+}
+
+bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, float* lse,
+                          const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t w0, int32_t w_pretrained, double theta,
+                          float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
+                          bf_stream stream) {
+  return prefill_impl(Q, K, V, O, lse, cu_seqlens, B, Hq, Hkv, D, w0, w_pretrained, theta,
+                      softmax_scale, dt, ws, ws_bytes, stream, false);
+}
+
+bf_status bifocal_prefill_ie(const void* Q, const void* K, const void* V, void* O, float* lse,
+                             const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t w0, int32_t w_pretrained, double theta,
+                             float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
+                             bf_stream stream) {
+  return prefill_impl(Q, K, V, O, lse, cu_seqlens, B, Hq, Hkv, D, w0, w_pretrained, theta,
+                      softmax_scale, dt, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -57,7 +57,14 @@ inline size_t table_row_bytes(int D) { return (size_t)(D / 2) * 2 * sizeof(float
 
 // Op scratch: decode partials (the larger of one sequence's vector path partials and
 // nseq sequences' matrix-core partials), or prefill pair maxima + selected pairs.
+// fp32 intermediates of the three inclusion-exclusion passes: O_x [T, Hq, D] and
+// LSE_x [Hq, T] for x = A, B, C.
+inline size_t ie_bytes(int64_t T, int Hq, int D) {
+  return 3 * (align_up((size_t)T * Hq * D * sizeof(float), 256) +
+              align_up((size_t)Hq * T * sizeof(float), 256));
+}
 inline size_t scratch_bytes(int op, int Hq, int Hkv, int D, int64_t nseq = 1) {
+  if (op == 3) op = 1;  // the inclusion-exclusion prefill shares the prefill scratch
   if (op == 2) {
     if (nseq < 1) nseq = 1;
     const size_t vec = (size_t)Hq * kDecodeMaxSplits * (D + 2) * sizeof(float);
@@ -97,7 +104,8 @@ inline WsLayout ws_layout(int op, int Hq, int Hkv, int D, size_t ws_bytes, size_
 
 inline size_t ws_bytes_for(int op, int max_len, int64_t total, int64_t num_seqs, int Hq, int Hkv,
                            int D) {
-  const size_t rec = op == 1 ? records_bytes(Hkv, max_tiles(total, num_seqs)) : 0;
+  size_t rec = (op == 1 || op == 3) ? records_bytes(Hkv, max_tiles(total, num_seqs)) : 0;
+  if (op == 3) rec += ie_bytes(total, Hq, D);
   return 256 + align_up((size_t)max_len * table_row_bytes(D), 256) + rec +
          scratch_bytes(op, Hq, Hkv, D, op == 2 ? num_seqs : 1);
 }

@@ -40,7 +40,13 @@ struct PrefillArgs {
   uint8_t* rec;        // key-tile records [Hkv][tiles_total] (bf16 path)
   int32_t T, Hq, Hkv, D, w0, nseq, max_qblocks, tiles_total;
   float scale;         // softmax scale (natural-log domain)
-  float pad1;
+  // Pair set and score rule of the launch: 0 = bifocal (each causal pair by its own
+  // rule); the three passes of the inclusion-exclusion form: 1 = remote scores over
+  // all causal pairs, 2 = remote scores over the window pairs, 3 = local scores over
+  // the window pairs.
+  int32_t mode;
+  int32_t out_f32;     // O written as float32 (the passes' intermediates) instead of dtype
+  int32_t pad1;
   SeqInfo seq[kMaxSeqPerLaunch];
 };
 

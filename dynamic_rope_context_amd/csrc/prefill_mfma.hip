@@ -169,7 +169,9 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
     *reinterpret_cast<uint4*>(&sv[k][8 * p]) = v0;
     *reinterpret_cast<uint4*>(&sv[k][64 + 8 * p]) = v1;
   }
-  if (G > 1) {  // G = 1: every pair is local, the remote copy is never read
+  // G = 1 in the bifocal mode: every pair is local, the remote copy is never read (the
+  // inclusion-exclusion passes read it whatever G is)
+  if (G > 1 || args.mode != 0) {
     uint4 y1p = zero, y2p = zero;
     if (valid) {
       const uint4 a = *reinterpret_cast<const uint4*>(Kp + row_off + 8 * p);
@@ -287,8 +289,10 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const DivMagic gdiv{args.seq[b].gmul, args.seq[b].gshift};
   const int Hq = args.Hq;
   const int i_end = min(L, i0 + BMPOS);  // exclusive
-  // G = 1: the aliased positions are the true ones, every pair is "local".
-  const int w0 = G == 1 ? (1 << 30) : args.w0;
+  const int mode = args.mode;
+  // G = 1: the aliased positions are the true ones, every pair is "local".  The
+  // remote-over-all-causal-pairs pass classifies with w0 = 0 (every pair remote).
+  const int w0 = mode == 0 ? (G == 1 ? (1 << 30) : args.w0) : (mode == 1 ? 0 : args.w0);
 
   const uint16_t* __restrict__ Qp = (const uint16_t*)args.Q;
   const uint16_t* __restrict__ Kp = (const uint16_t*)args.K;
@@ -305,7 +309,9 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // [ktA,ktB) straddle the window edge.  The block walks a sequence of virtual tiles:
   // a remote pass over [0,ktB), then a local pass over [ktA,nkt); on straddling tiles
   // each pass masks the pairs of the other class, so every pair is scored once, by its
-  // own rule, in one online softmax.
+  // own rule, in one online softmax.  The inclusion-exclusion passes walk: remote over
+  // [0,nkt) with causal masks (mode 1), remote over the window tiles [ktA,nkt) with the
+  // window mask (mode 2), local over [ktA,nkt) (mode 3).
   const int nkt = (i_end - 1) / BK + 1;
   int ktA, ktB;
   {
@@ -316,8 +322,12 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     ktA = min(ktA, nkt);
     ktB = min(max(ktB, ktA), nkt);
   }
-  const int nvt = ktB + (nkt - ktA);
-  auto vt_kt = [&](int v) __attribute__((always_inline)) { return v < ktB ? v : ktA + (v - ktB); };
+  // remote pass: physical tiles [r0, r0 + nr); local pass: [ktA, ktA + nl)
+  const int r0 = mode == 2 ? ktA : 0;
+  const int nr = mode == 0 ? ktB : (mode == 3 ? 0 : nkt - r0);
+  const int nl = (mode == 0 || mode == 3) ? nkt - ktA : 0;
+  const int nvt = nr + nl;
+  auto vt_kt = [&](int v) __attribute__((always_inline)) { return v < nr ? r0 + v : ktA + (v - nr); };
 
   // ---- query operands -------------------------------------------------------------
   // B operand of S^T = K Q^T: lane (column ln, half hf) holds channels 16s + 8hf + e.
@@ -389,7 +399,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     const int kt = vt_kt(v);
     uint8_t* st = smem_raw + so;
     const uint8_t* rec = rec_seq + (size_t)kt * kRecBytes;
-    if (v < ktB) {
+    if (v < nr) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (q == 0 || wave == 0)
@@ -502,12 +512,12 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // closing iteration v, tile v+2 must have landed: the younger transfers (tiles v+3 ..
   // v+PREF, at least two per tile) may still be in flight.
   constexpr int kVmAhead = 2 * (PREF - 2);
-  if (ktB > 0) load_q_remote();
+  if (nr > 0) load_q_remote();
   else load_q_std();
 #pragma unroll
   for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes);
   wait_vm_barrier<kVmAhead>();  // tiles 0 and 1 in LDS
-  f32x16 s_cur = ktB > 0 ? qk_remote(0) : qk_local(0);
+  f32x16 s_cur = nr > 0 ? qk_remote(0) : qk_local(0);
 
   // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
   // so its scores are computed unconditionally and simply unused past the end.  Two
@@ -545,18 +555,24 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   //   remote unmasked [0, ktA) | remote straddling [ktA, ktB) | local straddling
   //   | local unmasked | local diagonal; the last remote tile switches the query operand.
   const int kt_diag = i0 >= BK - 1 ? (i0 - (BK - 1)) / BK + 1 : 0;  // first diagonal tile
-  const int v_loc_plain = ktB + (ktB - ktA);           // first local tile past the window edge
-  const int v_diag = ktB + (max(kt_diag, ktA) - ktA);  // first local tile needing causality
+  const int v_loc_plain = nr + (ktB - ktA);           // first local tile past the window edge
+  const int v_diag = nr + (max(kt_diag, ktA) - ktA);  // first local tile needing causality
+  const int v_rem_mask = ktA - r0;                    // first remote tile needing a mask
   int v = 0;
-  run(v, min(ktA, ktB - 1), kRem(), kNoMask());
-  run(v, ktB - 1, kRem(), kRemMask());
-  if (ktB > 0) {  // last remote tile: the next scores are local
+  if (mode == 2) {
+    run(v, nr - 1, kRem(), kLocMask());
+  } else {
+    run(v, min(v_rem_mask, nr - 1), kRem(), kNoMask());
+    run(v, nr - 1, kRem(), kRemMask());
+  }
+  if (nr > 0) {  // last remote tile: the next scores are local (or past the end)
     load_q_std();
-    if (v >= ktA) run(v, v + 1, kLoc(), kRemMask());
+    if (mode == 2) run(v, v + 1, kLoc(), kLocMask());
+    else if (v >= v_rem_mask) run(v, v + 1, kLoc(), kRemMask());
     else run(v, v + 1, kLoc(), kNoMask());
   }
   run(v, min(v_loc_plain, nvt), kLoc(), kLocMask());
-  run(v, v_diag, kLoc(), kNoMask());
+  run(v, min(v_diag, nvt), kLoc(), kNoMask());
   run(v, nvt, kLoc(), kLocMask());
   // Transfers issued past the last tile must land before this workgroup's LDS is
   // handed to another one.
@@ -567,17 +583,31 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qi < L) {
     const float inv = 1.f / l_tot;
-    uint16_t* orow = (uint16_t*)args.O + ((size_t)(start + qi) * Hq + qhead) * D;
+    const size_t orow_off = ((size_t)(start + qi) * Hq + qhead) * D;
+    if (args.out_f32) {
+      float* orow = (float*)args.O + orow_off;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * hf;
-        const f32x16& o = oacc[db];
-        *reinterpret_cast<uint2*>(orow + d) =
-            make_uint2(pack_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
-                       pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * db + 8 * q4 + 4 * hf;
+          const f32x16& o = oacc[db];
+          *reinterpret_cast<float4*>(orow + d) = make_float4(o[4 * q4] * inv, o[4 * q4 + 1] * inv,
+                                                             o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv);
+        }
+    } else {
+      uint16_t* orow = (uint16_t*)args.O + orow_off;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * db + 8 * q4 + 4 * hf;
+          const f32x16& o = oacc[db];
+          *reinterpret_cast<uint2*>(orow + d) =
+              make_uint2(pack_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
+                         pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
+        }
+    }
     if (args.lse && hf == 0)
       args.lse[(size_t)qhead * args.T + start + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }

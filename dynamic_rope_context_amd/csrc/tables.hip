@@ -32,13 +32,18 @@ __global__ void __launch_bounds__(256) table_ensure_kernel(TableHeader* hdr, flo
   __syncthreads();
   if (s_skip) return;
 
+  // theta_m once per block (D/2 <= 128 values): a float64 pow per entry would cost
+  // more than the sine and cosine together
+  __shared__ double s_invf[128];
   const int half = D / 2;
+  for (int m = threadIdx.x; m < half; m += blockDim.x) s_invf[m] = inv_freq64(theta, m, D);
+  __syncthreads();
   const size_t total = (size_t)n_build * half;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
     const int p = (int)(idx / half);
     const int m = (int)(idx - (size_t)p * half);
-    const double a = (double)p * inv_freq64(theta, m, D);
+    const double a = (double)p * s_invf[m];
     double s, c;
     sincos_reduced(a, &s, &c);
     tab[idx] = make_float2((float)c, (float)s);

@@ -53,7 +53,7 @@ typedef enum {
 
 typedef enum { BF_F32 = 0, BF_BF16 = 1 } bf_dtype;
 
-typedef enum { BF_OP_ROPE = 0, BF_OP_PREFILL = 1, BF_OP_DECODE = 2 } bf_op;
+typedef enum { BF_OP_ROPE = 0, BF_OP_PREFILL = 1, BF_OP_DECODE = 2, BF_OP_PREFILL_IE = 3 } bf_op;
 
 /* HIP stream handle; 0 is the default stream. */
 typedef struct ihipStream_t* bf_stream;
@@ -105,6 +105,30 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
                           int32_t D, int32_t w0, int32_t w_pretrained, double theta,
                           float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
                           bf_stream stream);
+
+/*
+ * bifocal_prefill_ie -- the same attention as bifocal_prefill, computed literally as
+ * the pages' three passes merged by inclusion-exclusion of their LogSumExp statistics
+ * (section 1): A = local scores over the window pairs (0 <= i - j < w0), B = remote
+ * scores over all causal pairs, C = remote scores over the window pairs; then
+ *   Z = e^{LSE_B} - e^{LSE_C} + e^{LSE_A},
+ *   O = (e^{LSE_B} O_B - e^{LSE_C} O_C + e^{LSE_A} O_A) / Z,   lse = ln Z.
+ *   The passes run the bf16 matrix-core kernel in three modes and keep O_x in fp32;
+ *   a merge kernel forms O (bf16) and lse.  Meant for measuring the fused selection
+ *   against the literal form and for cross-checking it; bifocal_prefill is faster.
+ *   Arguments, layouts and errors as for bifocal_prefill; dt must be BF_BF16
+ *   (BF_EUNSUPPORTED otherwise).  Where Z_B and Z_C nearly cancel, the merge loses
+ *   the corresponding relative precision (not so for rows whose causal keys all lie
+ *   in the window: there passes B and C are bitwise equal and O = O_A).
+ *   ws, ws_bytes: workspace of at least
+ *     bifocal_workspace_bytes(BF_OP_PREFILL_IE, max_b L_b, T, B, Hq, Hkv, D), which adds
+ *     3 * (T * Hq * D + Hq * T) floats of intermediates to the prefill workspace.
+ */
+bf_status bifocal_prefill_ie(const void* Q, const void* K, const void* V, void* O, float* lse,
+                             const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t w0, int32_t w_pretrained, double theta,
+                             float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
+                             bf_stream stream);
 
 /*
  * bifocal_decode -- one generation step over a standard-RoPE KV cache.
@@ -161,7 +185,7 @@ bf_status bifocal_decode_batch(const void* q, const void* Kcache, const void* Vc
 /*
  * bifocal_workspace_bytes -- workspace size for an operation.
  *   max_len: the longest sequence a prefill will see, or the largest pos + 1 for decode.
- *   total_tokens, num_seqs: prefill: the largest T and B of the calls that will use the
+ *   total_tokens, num_seqs: prefill (both ops): the largest T and B of the calls that will use the
  *     workspace (max_len <= total_tokens <= num_seqs * max_len).  Decode: num_seqs is the
  *     largest batch B (0 counts as 1), total_tokens is ignored.
  *   Returns 0 for invalid arguments.

@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 
 import workloads
-from oracle.bifocal_ref import rope_rotate
+from oracle.bifocal_ref import alias, group_size, rope_rotate
 
 BF16_TOL = dict(max_abs=2e-2, mean_abs=2e-3, lse_abs=5e-3)
 F32_TOL = dict(max_abs=1e-4)
@@ -66,3 +66,43 @@ def errors(o_gpu, o_ref, lse_gpu=None, lse_ref=None):
 
 def within(err: dict, tol: dict) -> bool:
     return all(err[k] <= v for k, v in tol.items() if k in err)
+
+
+def ie_conditioning(Q_std, K_std, rows, w0: int, w_pretrained: int, theta: float,
+                    scale=None, key_block: int = 16384) -> np.ndarray:
+    """Conditioning of the three-pass inclusion-exclusion merge at the given rows of one
+    sequence: max(1, Z_B / Z) per (row, query head), with Z_B the remote-score sum over
+    all causal keys and Z the bifocal sum (Z = Z_B - Z_C + Z_A).  Errors of the passes
+    (relative to their own sums) reach the merged result multiplied by this factor.
+    Computed in float64 from the oracle's rotations; returns [len(rows), Hq]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    L, Hq, D = Q_std.shape
+    Hkv = K_std.shape[1]
+    rep = Hq // Hkv
+    sc = 1.0 / np.sqrt(D) if scale is None else scale
+    G = group_size(L, w_pretrained)
+    n_all = alias(np.arange(L), G) - np.arange(L)
+    Qs = np.asarray(Q_std[rows], dtype=np.float64)
+    Qr = rope_rotate(Qs, n_all[rows], theta)
+    out = np.empty((len(rows), Hq))
+    for g in range(Hkv):
+        qs = Qs[:, g * rep:(g + 1) * rep].reshape(-1, D)
+        qr = Qr[:, g * rep:(g + 1) * rep].reshape(-1, D)
+        ri = np.repeat(rows, rep)
+        lse = {k: np.full(len(ri), -np.inf) for k in "ABCZ"}
+        for j0 in range(0, L, key_block):
+            j1 = min(L, j0 + key_block)
+            ks = np.asarray(K_std[j0:j1, g], dtype=np.float64)
+            kr = rope_rotate(np.asarray(K_std[j0:j1, g:g + 1]), n_all[j0:j1], theta)[:, 0]
+            s_loc = sc * qs @ ks.T
+            s_rem = sc * qr @ kr.T
+            dist = ri[:, None] - np.arange(j0, j1)[None, :]
+            causal = dist >= 0
+            win = causal & (dist < w0)
+            for k, s_, m_ in (("A", s_loc, win), ("B", s_rem, causal), ("C", s_rem, win),
+                              ("Z", np.where(win, s_loc, s_rem), causal)):
+                x = np.where(m_, s_, -np.inf)
+                lse[k] = np.logaddexp(lse[k], np.logaddexp.reduce(x, axis=1))
+        out[:, g * rep:(g + 1) * rep] = np.maximum(1.0, np.exp(lse["B"] - lse["Z"])).reshape(
+            len(rows), rep)
+    return out

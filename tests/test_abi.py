@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("bifocal_prefill", "bifocal_decode", "rope_apply", "bifocal_workspace_bytes",
-              "bifocal_status_string", "bifocal_group_size"):
+              "bifocal_status_string", "bifocal_group_size", "bifocal_prefill_ie",
+              "bifocal_decode_batch"):
         assert n in names
 
 
@@ -101,6 +102,31 @@ def test_prefill_rejects_bad_arguments_before_launch(lib):
     assert _prefill(lib, ws_bytes=4096) == BF_EWORKSPACE
     assert _prefill(lib, dt=7) == BF_EINVAL
     assert _prefill(lib, cu=[0, 0], Q=0) == BF_OK           # empty batch: nothing to do
+
+
+def test_prefill_ie_rejects_bad_arguments_before_launch(lib):
+    def call(**kw):
+        a = dict(Q=16, K=16, V=16, O=16, lse=0, B=1, Hq=4, Hkv=1, D=128, w0=4, w_pre=16,
+                 theta=1e4, scale=0.0, dt=1, ws=256, ws_bytes=1 << 30, cu=[0, 64])
+        a.update(kw)
+        arr = (ctypes.c_int32 * len(a["cu"]))(*a["cu"])
+        return lib.bifocal_prefill_ie(a["Q"], a["K"], a["V"], a["O"], a["lse"],
+                                      ctypes.cast(arr, ctypes.c_void_p), a["B"], a["Hq"],
+                                      a["Hkv"], a["D"], a["w0"], a["w_pre"], a["theta"],
+                                      a["scale"], a["dt"], a["ws"], a["ws_bytes"], None)
+    assert call(dt=0) == BF_EUNSUPPORTED      # the three-pass form is bf16 only
+    assert call(w0=0) == BF_EINVAL
+    assert call(Hq=12, Hkv=4) == BF_EUNSUPPORTED
+    assert call(ws=0) == BF_EWORKSPACE
+    assert call(ws_bytes=1 << 16) == BF_EWORKSPACE
+    assert call(cu=[0, 0], Q=0) == BF_OK
+
+
+def test_prefill_ie_workspace_adds_intermediates(lib):
+    one = lib.bifocal_workspace_bytes(1, 4096, 8192, 2, 32, 8, 128)
+    ie = lib.bifocal_workspace_bytes(3, 4096, 8192, 2, 32, 8, 128)
+    assert ie >= one + 3 * (8192 * 32 * 128 * 4 + 32 * 8192 * 4)
+    assert lib.bifocal_workspace_bytes(3, 4096, 100, 2, 32, 8, 128) == 0   # T < max_len
 
 
 def _decode(lib, **kw):

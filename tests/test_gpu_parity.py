@@ -11,8 +11,8 @@ import torch
 import workloads as W
 from oracle.bifocal_ref import (bifocal_decode_ref, bifocal_prefill_ref, group_size,
                                 rope_apply_ref, rope_rotate)
-from helpers import (BF16_TOL, F32_TOL, decode_inputs, errors, prefill_inputs, std_query,
-                     to_dtype, within)
+from helpers import (BF16_TOL, F32_TOL, decode_inputs, errors, ie_conditioning,
+                     prefill_inputs, std_query, to_dtype, within)
 
 pytestmark = pytest.mark.gpu
 
@@ -319,3 +319,56 @@ def test_decode_across_length_boundary(bf, dt):
         e = errors(host(o[k]), refs[i][0], lse[k].cpu().numpy(), refs[i][1])
         say(f"  batch member {k} pos={positions[i]} {e}")
         assert within(e, tol), (positions[i], e)
+
+
+# ---------------------------------------------------------------------------
+# the literal three-pass inclusion-exclusion form
+# ---------------------------------------------------------------------------
+
+IE_CASES = [c for c in BF16_CASES if c[0] in ("rep4_g4", "rep2_ragged", "rep8_w0_1", "rep4_g1",
+                                                "rep4_wide_window", "rep4_w0_ge_L")]
+
+
+@pytest.mark.parametrize("case", IE_CASES, ids=[c[0] for c in IE_CASES])
+def test_prefill_ie_matches_oracle_and_fused(bf, case):
+    # The merge Z = Z_B - Z_C + Z_A cancels where most of the remote mass lies in the
+    # window while the local scores there are small (outlier channels make that
+    # common): the passes' own errors (bf16 probabilities: relative 2^-9 per term) then
+    # grow by cond = Z_B / Z.  Rows with cond <= 1.5 (most of them) must meet the bf16
+    # tolerance; the others a bound that grows with cond.  A wrong pass would show in
+    # the well-conditioned rows.
+    name, Hq, Hkv, seqlens, w_pre, w0, outl = case
+    w = W.Workload(name, "prefill", "bf16", Hq=Hq, Hkv=Hkv, D=128, w0=w0, w_pretrained=w_pre,
+                   theta=1e6, seqlens=seqlens, outliers=outl, seed=700 + len(name))
+    say("prefill ie", w)
+    Q, K, V, cu = prefill_inputs(w)
+    cuts = [int(c) for c in cu]
+    Qd, Kd, Vd = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    O3, L3 = bf.bifocal_prefill_ie(Qd, Kd, Vd, cuts, w.w0, w.w_pretrained, w.theta)
+    O1, L1 = bf.bifocal_prefill(Qd, Kd, Vd, cuts, w.w0, w.w_pretrained, w.theta)
+    torch.cuda.synchronize()
+    O3, L3, O1, L1 = host(O3), L3.cpu().numpy(), host(O1), L1.cpu().numpy()
+    assert np.all(np.isfinite(O3)) and np.all(np.isfinite(L3))
+    ref = bifocal_prefill_ref(Q, K, V, cu, w.w0, w.w_pretrained, w.theta)
+    for b, (rows, O, LSE) in enumerate(ref):
+        if O is None:
+            continue
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        cond = ie_conditioning(Q[s0:s1], K[s0:s1], rows, w.w0, w.w_pretrained, w.theta)
+        good = cond <= 1.5  # [rows, Hq]
+        vmax = float(np.abs(V[s0:s1]).max())
+        d_o = np.abs(O3[s0 + rows].astype(np.float64) - O).max(axis=2)
+        d_l = np.abs(L3[:, s0 + rows].T - LSE)
+        d_of = np.abs(O3[s0 + rows].astype(np.float64) - O1[s0 + rows]).max(axis=2)
+        say(f"  seq {b}: cond max {cond.max():.3g}, {np.mean(good) * 100:.1f}% of (row, head) "
+            f"with cond <= 1.5; well-conditioned max |dO| {d_o[good].max():.3g} mean "
+            f"{np.abs(O3[s0 + rows] - O)[good].mean():.3g} max |dLSE| {d_l[good].max():.3g}; "
+            f"three-pass vs fused max |dO| {d_of[good].max():.3g}")
+        assert d_o[good].max() <= BF16_TOL["max_abs"]
+        assert np.abs(O3[s0 + rows] - O)[good].mean() <= BF16_TOL["mean_abs"]
+        assert d_l[good].max() <= BF16_TOL["lse_abs"]
+        assert d_of[good].max() <= BF16_TOL["max_abs"]
+        # everywhere: each pass's sums carry the bf16 rounding of its probabilities
+        # (relative 2^-8 at worst), which the merge scales by the conditioning
+        assert np.all(d_l <= BF16_TOL["lse_abs"] + 2.0 ** -7 * cond)
+        assert np.all(d_o <= BF16_TOL["max_abs"] + 2.0 ** -7 * cond * vmax)
