@@ -63,9 +63,14 @@ struct Stage {
   uint16_t vt[D * VT_LD];   // V^T, bf16 bits, swizzled chunks (see VT_LD)
 };
 static_assert(sizeof(Stage) == 18432, "stage = 18 KiB");
-constexpr int NSTAGE = 6;          // LDS ring of virtual tiles
-constexpr int PREF = NSTAGE - 1;   // tiles issued ahead of the one being computed
-constexpr size_t kSmem = NSTAGE * sizeof(Stage);
+constexpr int NSTAGE = 8;          // LDS ring of virtual tiles
+// Tiles issued ahead of the one being computed.  The workgroup meets at a barrier
+// after every second tile, so a slot is refilled two tiles after its last use.
+constexpr int PREF = NSTAGE - 2;
+// after the ring: each wave's hi/lo query operand of the remote pass (one 16-byte
+// chunk per lane), read back per tile instead of held in registers
+constexpr size_t kQcorOff = NSTAGE * sizeof(Stage);
+constexpr size_t kSmem = kQcorOff + NW * 64 * 16;
 
 }  // namespace mf
 
@@ -332,7 +337,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // ---- query operands -------------------------------------------------------------
   // B operand of S^T = K Q^T: lane (column ln, half hf) holds channels 16s + 8hf + e.
   u32x4 qop[8];   // remote pass: fp16 of R(f(i)-i) q; local pass: bf16 q
-  u32x4 qcor;     // hi (half 0) or lo (half 1) of the 8 selected remote channels
+  // hi (half 0) or lo (half 1) of the 8 selected remote channels, kept in LDS
+  u32x4* const qcor_lds = reinterpret_cast<u32x4*>(smem_raw + kQcorOff) + 64 * wave + lane;
   auto load_q_std = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
@@ -371,8 +377,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       part[p] = hf ? l1 : h1;
       part[p + 4] = hf ? l2 : h2;
     }
-    qcor = u32x4{part[0] | (part[1] << 16), part[2] | (part[3] << 16),
-                 part[4] | (part[5] << 16), part[6] | (part[7] << 16)};
+    *qcor_lds = u32x4{part[0] | (part[1] << 16), part[2] | (part[3] << 16),
+                      part[4] | (part[5] << 16), part[6] | (part[7] << 16)};
   };
 
   // ---- staging: LDS-DMA straight from the key-tile records / K rows ----------------
@@ -385,15 +391,21 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       args.rec + ((size_t)g * args.tiles_total + args.seq[b].tile_base) * kRecBytes;
   const uint16_t* kseq = Kp + ((size_t)start * Hkv + g) * D;
   const uint32_t krow_stride = (uint32_t)Hkv * D;  // elements between tokens
-  int kpos_r[2], kpos_c[2];  // padded row / chunk of this lane in transfers wave, 8
+  // Per lane of key transfers wave and 8: byte offset in a record (remote tiles) and
+  // the padded row / chunk (local tiles); addresses are a uniform base plus a 32-bit
+  // lane offset, which keeps no 64-bit pointers live per lane.
+  uint32_t krec_off[2], krow_r[2], kcol_b[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int p = 64 * (q == 0 ? wave : 8) + lane;
     const int r = p / 17, c = p % 17;
     const bool real = c < 16 && r < BK;
-    kpos_r[q] = real ? r : 0;
-    kpos_c[q] = real ? c : 0;
+    krow_r[q] = real ? r : 0;
+    kcol_b[q] = real ? 16 * c : 0;
+    krec_off[q] = krow_r[q] * 256 + kcol_b[q];
   }
+  const uint32_t lane16 = 16 * lane;
+  const uint32_t krow_bytes = 2 * krow_stride;
   auto issue = [&](int v, int so) __attribute__((always_inline)) {
     v = min(v, nvt - 1);  // past the end: repeat the last tile (keeps the vmcnt count)
     const int kt = vt_kt(v);
@@ -403,19 +415,18 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (q == 0 || wave == 0)
-          dma16(rec + (kpos_r[q] * 16 + kpos_c[q]) * 16,
-                st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
-      if (wave == 0) dma16(rec + kRecKr + 16 * lane, st + offsetof(Stage, kc));
+          dma16(rec + krec_off[q], st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
+      if (wave == 0) dma16(rec + kRecKr + lane16, st + offsetof(Stage, kc));
     } else {
+      const uint8_t* kb = reinterpret_cast<const uint8_t*>(kseq);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (q == 0 || wave == 0) {
-          const int j = min(kt * BK + kpos_r[q], L - 1);
-          dma16(kseq + (uint32_t)j * krow_stride + 8 * kpos_c[q],
-                st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
+          const uint32_t j = min((uint32_t)(kt * BK) + krow_r[q], (uint32_t)(L - 1));
+          dma16(kb + (j * krow_bytes + kcol_b[q]), st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
         }
     }
-    dma16(rec + kRecKr + kRecKc + 1024 * wave + 16 * lane, st + offsetof(Stage, vt) + 1024 * wave);
+    dma16(rec + (kRecKr + kRecKc + 1024 * wave) + lane16, st + offsetof(Stage, vt) + 1024 * wave);
   };
   constexpr int kStageBytes = (int)sizeof(Stage);
   auto slot = [&](int v) __attribute__((always_inline)) { return (v % NSTAGE) * kStageBytes; };
@@ -434,7 +445,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     for (int s = 0; s < 8; ++s)
       sacc = mfma_f16(*reinterpret_cast<const u32x4*>(krow + 16 * s), qop[s], sacc);
     const uint16_t* crow = st.kc + ln * KC_LD + 8 * (hf ^ ((ln >> 3) & 1));
-    return mfma_f16(*reinterpret_cast<const u32x4*>(crow), qcor, sacc);
+    return mfma_f16(*reinterpret_cast<const u32x4*>(crow), *qcor_lds, sacc);
   };
   auto qk_local = [&](int so) __attribute__((always_inline)) -> f32x16 {
     const Stage& st = *reinterpret_cast<const Stage*>(smem_raw + so);
@@ -507,16 +518,18 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   };
 
   // ---- software-pipelined loop over virtual tiles ----------------------------------
-  // Iteration v: virtual tiles v+2 .. v+PREF are in flight (LDS-DMA), v+1 is scored
-  // (MFMA) while v goes through the softmax (VALU) and PV (MFMA).  Before the barrier
-  // closing iteration v, tile v+2 must have landed: the younger transfers (tiles v+3 ..
-  // v+PREF, at least two per tile) may still be in flight.
-  constexpr int kVmAhead = 2 * (PREF - 2);
+  // Iteration v: later tiles are in flight (LDS-DMA), v+1 is scored (MFMA) while v
+  // goes through the softmax (VALU) and PV (MFMA).  The waves meet after odd
+  // iterations only: the barrier closing iteration v (odd) must see tiles up to v+3
+  // landed (read in iterations v+1 and v+2); the younger transfers (tiles v+4 ..
+  // v+PREF, at least two per tile) may still be in flight.  Iteration v refills the
+  // slot of tile v-2, whose last reader (iteration v-2) is behind a barrier.
+  constexpr int kVmAhead = 2 * (PREF - 3);
   if (nr > 0) load_q_remote();
   else load_q_std();
 #pragma unroll
   for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes);
-  wait_vm_barrier<kVmAhead>();  // tiles 0 and 1 in LDS
+  wait_vm_barrier<kVmAhead>();  // tiles 0 .. 2 in LDS
   f32x16 s_cur = nr > 0 ? qk_remote(0) : qk_local(0);
 
   // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
@@ -532,7 +545,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     uint32_t pk[8];
     softmax_exp(sc, pk);
     pv(pk, slot(v));
-    wait_vm_barrier<kVmAhead>();
+    if (v & 1) wait_vm_barrier<kVmAhead>();
   };
   f32x16 s_alt;
   auto run = [&](int& v, int end, auto qkrem_c, auto mk_c) __attribute__((always_inline)) {
