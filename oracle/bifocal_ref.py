@@ -42,6 +42,16 @@ documented constant here):
 * The softmax scale defaults to 1/sqrt(D); LSE is the natural log of the sum of
   exp(scaled scores).
 
+Variants (``variant`` argument; the default is the method itself):
+
+* ``"interp"``: the remote branch uses the continuous positions x / G instead of
+  floor(x / G): frequency interpolation in the style the pages' ablation compares
+  against ("aliasing vs interpolation", in the experimental results).  Everything
+  else (window, softmax) is unchanged.
+* ``"window"``: only the local window is attended (0 <= i - j < w0, classic RoPE),
+  the shape of the sliding-window layers of hybrid models the pages mention
+  (Jet-Nemotron); the remote pairs are dropped rather than re-scored.
+
 Parity pins (tests/test_oracle.py): brute force with explicit rotation
 matrices on tiny inputs; the three-pass inclusion-exclusion identity; G = 1
 equals vanilla causal RoPE attention (torch SDPA, float64); w0 = 1 equals pure
@@ -129,10 +139,21 @@ def rope_tables_ref(n_pos: int, D: int, theta: float, G: int):
 # Bifocal attention: per-pair routed softmax (Methodology sections 1 and 2)
 # ---------------------------------------------------------------------------
 
+VARIANTS = ("bifocal", "interp", "window")
+
+
+def _remote_positions(x, G: int, variant: str):
+    """Positions of the remote branch: floor(x / G) (the method) or x / G ("interp")."""
+    x = np.asarray(x, dtype=np.int64)
+    if variant == "interp":
+        return x.astype(np.float64) / G
+    return alias(x, G)
+
+
 def bifocal_rows(Q_std: np.ndarray, K_std: np.ndarray, V: np.ndarray, rows, w0: int,
                  w_pretrained: int, theta: float, scale: Optional[float] = None,
                  q_offset: int = 0, row_block: int = 64, heads: Optional[Sequence[int]] = None,
-                 L: Optional[int] = None, q_given_rows: bool = False
+                 L: Optional[int] = None, q_given_rows: bool = False, variant: str = "bifocal"
                  ) -> Tuple[np.ndarray, np.ndarray]:
     """Output and LSE of the selected query rows of ONE sequence.
 
@@ -150,6 +171,8 @@ def bifocal_rows(Q_std: np.ndarray, K_std: np.ndarray, V: np.ndarray, rows, w0: 
         raise ValueError("Hq must be a multiple of Hkv")
     if w0 < 1:
         raise ValueError("w0 must be >= 1")
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
     rep = Hq // Hkv
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     heads = list(range(Hq)) if heads is None else list(heads)
@@ -165,14 +188,14 @@ def bifocal_rows(Q_std: np.ndarray, K_std: np.ndarray, V: np.ndarray, rows, w0: 
     # Raw vectors: undo the standard RoPE carried by the inputs.
     k_raw = rope_rotate(K_std[:jmax, kv_heads], -pos, theta)
     k_loc = rope_rotate(k_raw, pos, theta)                 # classic RoPE at j
-    k_rem = rope_rotate(k_raw, alias(pos, G), theta)       # RoPE at f(j)
+    k_rem = rope_rotate(k_raw, _remote_positions(pos, G, variant), theta)  # RoPE at f(j)
     v = np.asarray(V[:jmax, kv_heads], dtype=np.float64)
     slot = {g: n for n, g in enumerate(kv_heads)}
 
     q_sel = np.asarray(Q_std if q_given_rows else Q_std[rows], dtype=np.float64)  # [R,Hq,D]
     q_raw = rope_rotate(q_sel, -rows, theta)
     q_loc = rope_rotate(q_raw, rows, theta)                # classic RoPE at i
-    q_rem = rope_rotate(q_raw, alias(rows, G) + q_offset, theta)   # RoPE at f(i)
+    q_rem = rope_rotate(q_raw, _remote_positions(rows, G, variant) + q_offset, theta)  # f(i)
 
     O = np.zeros((R, len(heads), D), dtype=np.float64)
     LSE = np.zeros((R, len(heads)), dtype=np.float64)
@@ -188,7 +211,7 @@ def bifocal_rows(Q_std: np.ndarray, K_std: np.ndarray, V: np.ndarray, rows, w0: 
             s_loc = q_loc[rb, h, :] @ k_loc[:, g, :].T
             s_rem = q_rem[rb, h, :] @ k_rem[:, g, :].T
             s = scale * np.where(local, s_loc, s_rem)
-            s = np.where(causal, s, -np.inf)
+            s = np.where(local if variant == "window" else causal, s, -np.inf)
             m = s.max(axis=1, keepdims=True)
             e = np.exp(s - m)
             z = e.sum(axis=1, keepdims=True)
@@ -199,7 +222,7 @@ def bifocal_rows(Q_std: np.ndarray, K_std: np.ndarray, V: np.ndarray, rows, w0: 
 
 def bifocal_prefill_ref(Q_std, K_std, V, cu_seqlens, w0: int, w_pretrained: int, theta: float,
                         scale: Optional[float] = None, rows_per_seq=None, heads=None,
-                        q_offset: int = 0):
+                        q_offset: int = 0, variant: str = "bifocal"):
     """Packed variable-length prefill: sequence b owns tokens cu[b] .. cu[b+1]-1 and
     local positions 0 .. L_b - 1; each sequence has its own G.
 
@@ -214,13 +237,14 @@ def bifocal_prefill_ref(Q_std, K_std, V, cu_seqlens, w0: int, w_pretrained: int,
             out.append((rows, None, None))
             continue
         O, LSE = bifocal_rows(Q_std[s:e], K_std[s:e], V[s:e], rows, w0, w_pretrained, theta,
-                              scale=scale, heads=heads, q_offset=q_offset)
+                              scale=scale, heads=heads, q_offset=q_offset, variant=variant)
         out.append((rows, O, LSE))
     return out
 
 
 def bifocal_decode_ref(q_std, K_cache, V_cache, pos: int, w0: int, w_pretrained: int,
-                       theta: float, scale: Optional[float] = None, heads=None):
+                       theta: float, scale: Optional[float] = None, heads=None,
+                       variant: str = "bifocal"):
     """One decode step: query at position ``pos`` over cache entries 0 .. pos,
     with G from the current length pos + 1.  q_std: [Hq, D] standard RoPE at pos;
     K_cache / V_cache: [S >= pos+1, Hkv, D] standard RoPE at absolute positions.
@@ -228,5 +252,5 @@ def bifocal_decode_ref(q_std, K_cache, V_cache, pos: int, w0: int, w_pretrained:
     L = int(pos) + 1
     O, LSE = bifocal_rows(np.asarray(q_std)[None], K_cache[:L], V_cache[:L], [pos], w0,
                           w_pretrained, theta, scale=scale, heads=heads, L=L,
-                          q_given_rows=True)
+                          q_given_rows=True, variant=variant)
     return O[0], LSE[0]

@@ -13,6 +13,8 @@ explicit D x D rotation matrices built entry by entry:
   floor(j/G)) otherwise, G = max(1, ceil(L / w_pretrained)) (technical
   summary, "Methodology" section 1).
 * Softmax over j <= i with an explicit running sum, LSE = ln(sum exp).
+* Variants: ``"interp"`` scores remote pairs at (i / G, j / G) as real numbers;
+  ``"window"`` keeps only the pairs with i - j < w0.
 
 Only meant for L up to a few dozen and D up to 8.
 """
@@ -38,7 +40,8 @@ def _matvec(Rm, x):
     return [sum(Rm[r][c] * x[c] for c in range(len(x))) for r in range(len(Rm))]
 
 
-def brute_attention(Q, K, V, w0: int, w_pretrained: int, theta: float, scale=None):
+def brute_attention(Q, K, V, w0: int, w_pretrained: int, theta: float, scale=None,
+                    variant: str = "bifocal"):
     """Q: nested lists [L][Hq][D]; K, V: [L][Hkv][D].  Returns (O [L][Hq][D], LSE [L][Hq])."""
     L = len(Q)
     Hq, D = len(Q[0]), len(Q[0][0])
@@ -56,9 +59,13 @@ def brute_attention(Q, K, V, w0: int, w_pretrained: int, theta: float, scale=Non
             q_raw = _matvec(_rot_matrix(-i, D, theta), Q[i][h])
             scores = []
             for j in range(i + 1):
+                if variant == "window" and i - j >= w0:
+                    continue
                 k_raw = _matvec(_rot_matrix(-j, D, theta), K[j][g])
                 if i - j < w0:
                     pi, pj = i, j
+                elif variant == "interp":
+                    pi, pj = i / G, j / G
                 else:
                     pi, pj = i // G, j // G
                 qv = _matvec(_rot_matrix(pi, D, theta), q_raw)
@@ -70,7 +77,8 @@ def brute_attention(Q, K, V, w0: int, w_pretrained: int, theta: float, scale=Non
                 tot += math.exp(s - mx)
             lse = mx + math.log(tot)
             LSE[i][h] = lse
-            for j, s in enumerate(scores):
+            js = [j for j in range(i + 1) if not (variant == "window" and i - j >= w0)]
+            for j, s in zip(js, scores):
                 w = math.exp(s - lse)
                 for d in range(D):
                     O[i][h][d] += w * V[j][g][d]

@@ -285,6 +285,84 @@ def test_inclusion_exclusion_three_pass_merge(L, w0, w_pre, scale_raw):
     assert np.all(np.abs(O - O_ie) <= 1e-11 * cond[..., None] * 10)
 
 
+# --------------------------------------------------------------------------
+# variants: continuous remote positions ("interp") and window-only layers
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["interp", "window"])
+@pytest.mark.parametrize("L,w0,w_pre", [(13, 3, 4), (16, 1, 5), (11, 12, 3), (14, 6, 14)])
+def test_variants_match_brute_force(variant, L, w0, w_pre):
+    Q, K, V = std_inputs(L, 4, 2, 8, 1e4, seed=L + 3 * w0)
+    Ob, Lb = brute.brute_attention(_to_lists(Q), _to_lists(K), _to_lists(V), w0, w_pre, 1e4,
+                                   variant=variant)
+    Oo, Lo = bifocal_rows(Q, K, V, np.arange(L), w0, w_pre, 1e4, variant=variant)
+    np.testing.assert_allclose(Oo, np.array(Ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Lo, np.array(Lb), rtol=0, atol=1e-12)
+
+
+def test_interp_with_g1_is_the_method():
+    # G = 1: x / G = floor(x / G) = x, both variants are vanilla RoPE attention
+    Q, K, V = std_inputs(60, 4, 2, 16, 1e4, seed=61)
+    O1, L1 = bifocal_rows(Q, K, V, np.arange(60), 7, 64, 1e4)
+    O2, L2 = bifocal_rows(Q, K, V, np.arange(60), 7, 64, 1e4, variant="interp")
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    np.testing.assert_allclose(O2, sdpa_f64(Q, K, V), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,w_pre,G", [(64, 16, 4), (90, 31, 3)])
+def test_interp_w0_one_equals_attention_at_scaled_positions(L, w_pre, G):
+    # w0 = 1: every off-diagonal pair is remote and scored at the real positions x / G;
+    # on the diagonal i/G - i/G = 0 = i - i.  So this is SDPA on inputs moved from x to
+    # x / G (rotation by x/G - x).
+    assert group_size(L, w_pre) == G
+    Q, K, V = std_inputs(L, 4, 1, 16, 1e4, seed=L + 5)
+    pos = np.arange(L)
+    Qs = rope_complex(Q, pos / G - pos, 1e4)
+    Ks = rope_complex(K, pos / G - pos, 1e4)
+    O, _ = bifocal_rows(Q, K, V, pos, w0=1, w_pretrained=w_pre, theta=1e4, variant="interp")
+    np.testing.assert_allclose(O, sdpa_f64(Qs, Ks, V), rtol=0, atol=1e-12)
+
+
+def test_interp_differs_from_aliasing_when_g_above_1():
+    # a planted-mistake guard: with G = 4 the two remote maps disagree
+    Q, K, V = std_inputs(48, 2, 1, 8, 1e4, seed=7)
+    O1, _ = bifocal_rows(Q, K, V, np.arange(48), 4, 12, 1e4)
+    O2, _ = bifocal_rows(Q, K, V, np.arange(48), 4, 12, 1e4, variant="interp")
+    assert np.max(np.abs(O1 - O2)) > 1e-3
+
+
+@pytest.mark.parametrize("L,w0", [(50, 9), (64, 1), (40, 40), (33, 100)])
+def test_window_equals_banded_sdpa(L, w0):
+    # window-only layer: SDPA with a banded causal mask (0 <= i - j < w0) on the inputs as
+    # given; w0 >= L is plain causal attention, w0 = 1 returns V_i
+    Q, K, V = std_inputs(L, 4, 2, 16, 1e4, seed=L * w0)
+    O, LSE = bifocal_rows(Q, K, V, np.arange(L), w0, 8, 1e4, variant="window")
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    band = torch.from_numpy((i - j >= 0) & (i - j < w0))
+    q = torch.from_numpy(np.ascontiguousarray(Q.transpose(1, 0, 2)))
+    k = torch.from_numpy(np.ascontiguousarray(np.repeat(K, 2, axis=1).transpose(1, 0, 2)))
+    v = torch.from_numpy(np.ascontiguousarray(np.repeat(V, 2, axis=1).transpose(1, 0, 2)))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=band)
+    np.testing.assert_allclose(O, ref.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+    if w0 == 1:
+        np.testing.assert_allclose(O, np.repeat(V, 2, axis=1), rtol=0, atol=1e-14)
+    if w0 >= L:
+        np.testing.assert_allclose(O, sdpa_f64(Q, K, V), rtol=0, atol=1e-12)
+
+
+def test_variant_decode_equals_prefill_row():
+    Q, K, V = std_inputs(120, 4, 2, 16, 1e4, seed=12)
+    for variant in ("interp", "window"):
+        for pos in (0, 17, 63, 119):
+            Od, Ld = bifocal_decode_ref(Q[pos], K, V, pos, w0=10, w_pretrained=30, theta=1e4,
+                                        variant=variant)
+            Op, Lp = bifocal_rows(Q[:pos + 1], K[:pos + 1], V[:pos + 1], [pos], 10, 30, 1e4,
+                                  variant=variant)
+            np.testing.assert_allclose(Od, Op[0], atol=1e-13)
+            np.testing.assert_allclose(Ld, Lp[0], atol=1e-13)
+
+
 def test_decode_equals_prefill_row():
     L = 150
     Q, K, V = std_inputs(L, 4, 2, 16, 1e4, seed=9)
