@@ -17,13 +17,15 @@ import torch
 __all__ = [
     "lib", "lib_path", "rope_apply", "bifocal_prefill", "bifocal_prefill_ie", "bifocal_decode",
     "bifocal_decode_batch", "workspace_bytes", "group_size", "Workspace", "BifocalError",
-    "OP_PREFILL", "OP_DECODE", "OP_PREFILL_IE",
+    "OP_PREFILL", "OP_DECODE", "OP_PREFILL_IE", "VARIANTS", "bifocal_prefill_variant",
+    "bifocal_decode_variant",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libbifocal.so")
 
 OP_ROPE, OP_PREFILL, OP_DECODE, OP_PREFILL_IE = 0, 1, 2, 3
+VARIANTS = {"bifocal": 0, "interp": 1, "window": 2}
 _F32, _BF16 = 0, 1
 
 
@@ -45,6 +47,12 @@ def _load():
     lib.bifocal_prefill.restype = i32
     lib.bifocal_prefill_ie.argtypes = lib.bifocal_prefill.argtypes
     lib.bifocal_prefill_ie.restype = i32
+    lib.bifocal_prefill_variant.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            f64, f32, i32, i32, vp, sz, vp]
+    lib.bifocal_prefill_variant.restype = i32
+    lib.bifocal_decode_variant.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           i32, f64, f32, i32, i32, vp, sz, vp]
+    lib.bifocal_decode_variant.restype = i32
     lib.bifocal_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f32,
                                    i32, vp, sz, vp]
     lib.bifocal_decode.restype = i32
@@ -258,4 +266,59 @@ def bifocal_decode_batch(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Te
         Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale),
         _dtype_code(q), workspace.ptr, workspace.nbytes, _stream(stream)),
         "bifocal_decode_batch")
+    return out, lse
+
+
+def _variant_code(variant) -> int:
+    if variant not in VARIANTS:
+        raise BifocalError(f"unknown variant {variant!r}; one of {sorted(VARIANTS)}")
+    return VARIANTS[variant]
+
+
+def bifocal_prefill_variant(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                            cu_seqlens: Sequence[int], w0: int, w_pretrained: int, theta: float,
+                            variant: str = "bifocal", softmax_scale: float = 0.0,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            want_lse: bool = True, workspace: Optional[Workspace] = None,
+                            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """bifocal_prefill for a variant: "bifocal", "interp" (remote positions x/G, continuous)
+    or "window" (local window only)."""
+    code = _variant_code(variant)
+    f = lib().bifocal_prefill_variant
+
+    def fn(*a):  # insert the variant before the dtype argument
+        return f(*a[:14], code, *a[14:])
+    return _prefill(fn, OP_PREFILL, Q, K, V, cu_seqlens, w0, w_pretrained, theta, softmax_scale,
+                    out, lse, want_lse, workspace, stream, "bifocal_prefill_variant")
+
+
+def bifocal_decode_variant(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor,
+                           pos: Sequence[int], w0: int, w_pretrained: int, theta: float,
+                           variant: str = "bifocal", softmax_scale: float = 0.0,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           want_lse: bool = True, workspace: Optional[Workspace] = None,
+                           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """bifocal_decode_batch for a variant (see bifocal_prefill_variant)."""
+    code = _variant_code(variant)
+    if q.dim() != 3 or Kcache.dim() != 4 or Vcache.shape != Kcache.shape:
+        raise BifocalError("expected q [B,Hq,D], Kcache and Vcache [B,S,Hkv,D]")
+    B, Hq, D = q.shape
+    S, Hkv = Kcache.shape[1], Kcache.shape[2]
+    pl = [int(p) for p in pos]
+    if len(pl) != B or Kcache.shape[0] != B or Kcache.shape[3] != D:
+        raise BifocalError("q, caches and pos disagree on the batch")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
+                                     num_seqs=max(B, 1))
+    pos_arr = (ctypes.c_int32 * max(B, 1))(*pl)
+    _check(lib().bifocal_decode_variant(
+        _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else 0, ctypes.cast(pos_arr, ctypes.c_void_p), B, S,
+        Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale), code,
+        _dtype_code(q), workspace.ptr, workspace.nbytes, _stream(stream)),
+        "bifocal_decode_variant")
     return out, lse

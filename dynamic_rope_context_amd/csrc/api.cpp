@@ -100,7 +100,8 @@ bf_status ensure_table(void* ws, const WsLayout& lay, int D, double theta, int n
 bf_status prefill_impl(const void* Q, const void* K, const void* V, void* O, float* lse,
                        const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                        int32_t w0, int32_t w_pretrained, double theta, float softmax_scale,
-                       bf_dtype dt, void* ws, size_t ws_bytes, bf_stream stream, bool ie) {
+                       bf_dtype dt, void* ws, size_t ws_bytes, bf_stream stream, bool ie,
+                       int32_t variant = BF_VARIANT_BIFOCAL) {
   if (!cu_seqlens || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || w0 < 1 || w_pretrained < 1 ||
       !(theta > 0.0) || !std::isfinite(theta) || !std::isfinite(softmax_scale))
     return BF_EINVAL;
@@ -121,6 +122,8 @@ bf_status prefill_impl(const void* Q, const void* K, const void* V, void* O, flo
   if (dt == BF_BF16 && (D != 128 || (rep != 1 && rep != 2 && rep != 4 && rep != 8)))
     return BF_EUNSUPPORTED;
   if (ie && dt != BF_BF16) return BF_EUNSUPPORTED;
+  if (variant < BF_VARIANT_BIFOCAL || variant > BF_VARIANT_WINDOW) return BF_EINVAL;
+  if (variant != BF_VARIANT_BIFOCAL && dt != BF_BF16) return BF_EUNSUPPORTED;
   if (T == 0) return BF_OK;
   if (!Q || !K || !V || !O) return BF_EINVAL;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
@@ -166,6 +169,9 @@ bf_status prefill_impl(const void* Q, const void* K, const void* V, void* O, flo
   a.D = D;
   a.w0 = w0;
   a.scale = softmax_scale > 0.f ? softmax_scale : (float)(1.0 / std::sqrt((double)D));
+  a.theta = theta;
+  a.interp = variant == BF_VARIANT_INTERP ? 1 : 0;
+  a.mode = variant == BF_VARIANT_WINDOW ? 3 : 0;  // window-only: the local pass alone
   // inclusion-exclusion intermediates (pass A: local/window, B: remote/causal,
   // C: remote/window), after the records
   float* ie_o[3] = {nullptr, nullptr, nullptr};
@@ -278,6 +284,15 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
                       softmax_scale, dt, ws, ws_bytes, stream, false);
 }
 
+bf_status bifocal_prefill_variant(const void* Q, const void* K, const void* V, void* O, float* lse,
+                                  const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t D, int32_t w0, int32_t w_pretrained, double theta,
+                                  float softmax_scale, int32_t variant, bf_dtype dt, void* ws,
+                                  size_t ws_bytes, bf_stream stream) {
+  return prefill_impl(Q, K, V, O, lse, cu_seqlens, B, Hq, Hkv, D, w0, w_pretrained, theta,
+                      softmax_scale, dt, ws, ws_bytes, stream, false, variant);
+}
+
 bf_status bifocal_prefill_ie(const void* Q, const void* K, const void* V, void* O, float* lse,
                              const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
                              int32_t D, int32_t w0, int32_t w_pretrained, double theta,
@@ -296,13 +311,15 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
                       const int32_t* pos, int32_t B, int64_t S, int32_t Hq, int32_t Hkv,
                       int32_t D, int32_t w0, int32_t w_pretrained, double theta,
                       float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
-                      bf_stream stream) {
+                      bf_stream stream, int32_t variant = BF_VARIANT_BIFOCAL) {
   if (B < 0 || (B > 0 && (!q || !Kcache || !Vcache || !o || !pos)) || S < 1 || Hq < 1 ||
       Hkv < 1 || Hq % Hkv || w0 < 1 || w_pretrained < 1 || !(theta > 0.0) ||
       !std::isfinite(theta) || !std::isfinite(softmax_scale))
     return BF_EINVAL;
   if (dt != BF_F32 && dt != BF_BF16) return BF_EINVAL;
+  if (variant < BF_VARIANT_BIFOCAL || variant > BF_VARIANT_WINDOW) return BF_EINVAL;
   if (D != 64 && D != 128) return BF_EUNSUPPORTED;
+  if (variant != BF_VARIANT_BIFOCAL && (dt != BF_BF16 || D != 128)) return BF_EUNSUPPORTED;
   const int rep = Hq / Hkv;
   if (rep != 1 && rep != 2 && rep != 4 && rep != 8) return BF_EUNSUPPORTED;
   int32_t max_pos = -1;
@@ -344,11 +361,14 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
     a.Hkv = Hkv;
     a.w0 = w0;
     a.scale_log2 = scale_log2;
+    a.variant = variant;
     for (int32_t b0 = 0; b0 < B; b0 += kDecodeMaxBatch) {
       const int nb = std::min<int32_t>(kDecodeMaxBatch, B - b0);
       int32_t mp = 0;
       for (int i = 0; i < nb; ++i) mp = std::max(mp, pos[b0 + i]);
-      const int64_t nblk = mp / 16 + 1;
+      // key blocks per sequence (window-only: those of the last w0 keys)
+      const int64_t nblk = variant == BF_VARIANT_WINDOW ? std::min<int64_t>(mp, w0) / 16 + 2
+                                                        : mp / 16 + 1;
       int64_t nwg = (512 + (int64_t)nb * Hkv - 1) / ((int64_t)nb * Hkv);
       nwg = std::min<int64_t>(nwg, std::max<int64_t>(1, nblk / (4 * 8)));
       nwg = std::max<int64_t>(1, std::min<int64_t>(nwg, kDecodeMaxParts));
@@ -359,7 +379,7 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
       for (int i = 0; i < nb; ++i) {
         const int32_t G = group_size((int64_t)pos[b0 + i] + 1, w_pretrained);
         const DivMagic m = div_magic((uint32_t)G);
-        a.seq[i] = DecSeq{pos[b0 + i], m.mul, m.shift, 0};
+        a.seq[i] = DecSeq{pos[b0 + i], m.mul, m.shift, G};
       }
       if (launch_decode_mfma(a, rep, st) != hipSuccess) return BF_EHIP;
     }
@@ -414,6 +434,15 @@ bf_status bifocal_decode(const void* q, const void* Kcache, const void* Vcache, 
   if (pos < 0 || pos == INT32_MAX) return BF_EINVAL;
   return decode_impl(q, Kcache, Vcache, o, lse, &pos, 1, (int64_t)pos + 1, Hq, Hkv, D, w0,
                      w_pretrained, theta, softmax_scale, dt, ws, ws_bytes, stream);
+}
+
+bf_status bifocal_decode_variant(const void* q, const void* Kcache, const void* Vcache, void* o,
+                                 float* lse, const int32_t* pos, int32_t B, int32_t S, int32_t Hq,
+                                 int32_t Hkv, int32_t D, int32_t w0, int32_t w_pretrained,
+                                 double theta, float softmax_scale, int32_t variant, bf_dtype dt,
+                                 void* ws, size_t ws_bytes, bf_stream stream) {
+  return decode_impl(q, Kcache, Vcache, o, lse, pos, B, S, Hq, Hkv, D, w0, w_pretrained, theta,
+                     softmax_scale, dt, ws, ws_bytes, stream, variant);
 }
 
 bf_status bifocal_decode_batch(const void* q, const void* Kcache, const void* Vcache, void* o,

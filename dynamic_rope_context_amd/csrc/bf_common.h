@@ -125,6 +125,13 @@ __device__ __forceinline__ void sincos_reduced(double a, double* s, double* c) {
   const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, a));
   sincos(r, s, c);
 }
+// (cos, sin) of the angle n * theta_m, formed and reduced in float64, rounded once
+// to float32 (the values a position-table row holds, for any real position n).
+__device__ __forceinline__ float2 angle_cs(double n, double invf) {
+  double s, c;
+  sincos_reduced(n * invf, &s, &c);
+  return make_float2((float)c, (float)s);
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

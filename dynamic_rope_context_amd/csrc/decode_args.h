@@ -26,8 +26,12 @@ struct DecSeq {
   int32_t pos;     // the query's position; keys 0 .. pos
   uint32_t gmul;   // floor(x / G) = (x * gmul) >> gshift, G from pos + 1
   uint32_t gshift;
-  int32_t pad;
+  int32_t G;
 };
+
+// Variants of the attention computed (decode and prefill): the method, continuous
+// remote positions x / G (frequency interpolation), or the local window alone.
+enum { kVariantBifocal = 0, kVariantInterp = 1, kVariantWindow = 2 };
 
 struct DecodeBatchArgs {
   const void* q;            // [B, Hq, D]
@@ -44,6 +48,7 @@ struct DecodeBatchArgs {
   int32_t nsplit, nwg;      // waves (splits) per (sequence, KV head); nwg = nsplit / 4
                             // workgroups, nwg <= kDecodeMaxParts
   float scale_log2;         // softmax scale * log2(e)
+  int32_t variant;          // kVariant*
   DecSeq seq[kDecodeMaxBatch];
 };
 

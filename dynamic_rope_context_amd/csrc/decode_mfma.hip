@@ -97,13 +97,6 @@ __device__ __forceinline__ float row_sum(float x) {
   return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));
 }
 
-// fp32 (cos, sin) of n * theta_m, rounded once from fp64.
-__device__ __forceinline__ float2 angle_cs(int n, double invf) {
-  double s, c;
-  sincos_reduced((double)n * invf, &s, &c);
-  return make_float2((float)c, (float)s);
-}
-
 template <int REP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeBatchArgs a) {
@@ -131,12 +124,18 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   const int w = wgi * NWD + wave;  // this wave's split
   const int pos = a.seq[bl].pos;
   const DivMagic gdiv{a.seq[bl].gmul, a.seq[bl].gshift};
-  const int nblk = pos / BK + 1;  // blocks holding keys 0 .. pos
+  const int variant = a.variant;
+  // continuous remote positions (interpolation variant): n(x) = x - x/G = x rpos
+  const double rpos = (double)(a.seq[bl].G - 1) / (double)a.seq[bl].G;
+  // window-only variant: keys from the block holding pos - w0 + 1
+  const int jb = variant == kVariantWindow ? (max(0, pos - a.w0 + 1) / BK) * BK : 0;
+  const int nblk = (pos - jb) / BK + 1;  // blocks holding keys jb .. pos
   const int nsplit = a.nsplit;
   // this wave's blocks: w, w + nsplit, w + 2 nsplit, ... < nblk
   const int cnt = w < nblk ? (nblk - 1 - w) / nsplit + 1 : 0;
 
-  const int last_remote = pos - a.w0;  // keys j <= last_remote are remote
+  // keys j <= last_remote are remote (none in the window-only variant)
+  const int last_remote = variant == kVariantWindow ? -1 : pos - a.w0;
   const float c2 = a.scale_log2;
   const uint32_t rs = (uint32_t)a.Hkv * D;  // elements between consecutive cache rows
   const uint16_t* kg = (const uint16_t*)a.K + (size_t)b * a.seq_stride + (size_t)g * D;
@@ -150,7 +149,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     uint4 v[2][2];
   };
   auto load_blk = [&](int i, Blk& x) __attribute__((always_inline)) {
-    const int j0 = (w + i * nsplit) * BK;
+    const int j0 = jb + (w + i * nsplit) * BK;
     const int jk = min(j0 + l16, pos);
     const uint16_t* kr = kg + (uint32_t)jk * rs + 8 * kq;
 #pragma unroll
@@ -180,8 +179,10 @@ decode_mfma_kernel(DecodeBatchArgs a) {
 
   // ---- angles: offset rows (shared) and the query's row --------------------------------
 #pragma unroll
-  for (int r = wave; r < BK; r += NWD) s_dt[r][lane] = angle_cs(r, invf);
-  row[lane] = angle_cs(pos - alias_fast(pos, gdiv), invf);
+  for (int r = wave; r < BK; r += NWD)
+    s_dt[r][lane] = angle_cs(variant == kVariantInterp ? r * rpos : (double)r, invf);
+  row[lane] = angle_cs(variant == kVariantInterp ? pos * rpos : (double)(pos - alias_fast(pos, gdiv)),
+                       invf);
 
   // ---- query operands (A: rows = query heads, lanes l16 >= REP zero) ------------------
   // lane (head l16, group kq) holds channels 32s + 8kq + e, s = 0..3
@@ -233,7 +234,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   uint16_t* pt = s_p[wave];
   // Blocks alternate between two load buffers (no register copy between blocks).
   auto block = [&](int i, const Blk& cur, Blk& nxt) __attribute__((always_inline)) {
-    const int j0 = (w + i * nsplit) * BK;  // <= pos
+    const int j0 = jb + (w + i * nsplit) * BK;  // <= pos
     const int jk = j0 + l16;
     const bool any_remote = j0 <= last_remote;
     const bool any_local = j0 + BK - 1 > last_remote;
@@ -263,11 +264,13 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
     if (any_remote) {
       const int jkc = min(jk, pos);
+      // n of the block's first key and the offset row of this lane's key: floor map
+      // (n steps by 0 or 1 per key) or continuous map (n = j rpos, offset row j - j0)
       const int n0 = j0 - alias_fast(j0, gdiv);
-      const int dk = (jkc - alias_fast(jkc, gdiv)) - n0;
+      const int dk = variant == kVariantInterp ? jkc - j0 : (jkc - alias_fast(jkc, gdiv)) - n0;
       // R(n0) of the block: lane = pair (the wave's previous reads of the row are
       // complete: LDS operations of a wave execute in order)
-      row[lane] = angle_cs(n0, invf);
+      row[lane] = angle_cs(variant == kVariantInterp ? j0 * rpos : (double)n0, invf);
       const float2* drow = &s_dt[dk][8 * kq];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -303,7 +306,8 @@ decode_mfma_kernel(DecodeBatchArgs a) {
       }
     }
     const bool use_local = pos - jk < a.w0;
-    const bool valid = jk <= pos;
+    // window-only variant: keys before the window are dropped, not re-scored
+    const bool valid = jk <= pos && (variant != kVariantWindow || use_local);
     float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = valid ? (use_local ? sl[r] : sr[r]) : -INFINITY;

@@ -38,6 +38,7 @@ struct PrefillArgs {
   const float2* tab;   // position table (cos, sin) [n][D/2]
   const int32_t* sel;  // [Hkv][kSelPairs] RoPE pairs given the hi/lo correction
   uint8_t* rec;        // key-tile records [Hkv][tiles_total] (bf16 path)
+  double theta;        // RoPE base (angles evaluated in the kernels: continuous positions)
   int32_t T, Hq, Hkv, D, w0, nseq, max_qblocks, tiles_total;
   float scale;         // softmax scale (natural-log domain)
   // Pair set and score rule of the launch: 0 = bifocal (each causal pair by its own
@@ -46,7 +47,9 @@ struct PrefillArgs {
   // the window pairs.
   int32_t mode;
   int32_t out_f32;     // O written as float32 (the passes' intermediates) instead of dtype
-  int32_t pad1;
+  // Remote positions: 0 = floor(x / G) (the method), 1 = x / G (continuous: the
+  // frequency-interpolation variant of the pages' ablation)
+  int32_t interp;
   SeqInfo seq[kMaxSeqPerLaunch];
 };
 

@@ -142,6 +142,7 @@ __global__ void pair_select_kernel(const uint32_t* __restrict__ mxq,
 __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
   using namespace mf;
   __shared__ __align__(16) uint16_t sv[BK][D + 8];
+  __shared__ double s_invf[D / 2];  // theta_m (continuous remote positions only)
   const int g = blockIdx.y;
   const int t_local = blockIdx.x;
   const int base0 = args.seq[0].tile_base;
@@ -164,6 +165,12 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
 
   const int tid = threadIdx.x;
   const int k = tid >> 3, p = tid & 7;  // key of the tile; pairs 8p .. 8p+7
+  const bool interp = args.interp != 0;
+  const double rpos = (double)(G - 1) / (double)G;  // continuous: n(x) = x - x/G = x rpos
+  if (interp) {
+    if (tid < D / 2) s_invf[tid] = inv_freq64(args.theta, tid, D);
+    __syncthreads();
+  }
   const int j = kt * BK + k;
   const bool valid = j < L;
   const size_t row_off = ((size_t)(start + min(j, L - 1)) * Hkv + g) * D;
@@ -186,7 +193,14 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
       float y1[8], y2[8];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const float4 cs = trow[e2];
+        float4 cs;
+        if (interp) {
+          const float2 c0 = angle_cs(j * rpos, s_invf[8 * p + 2 * e2]);
+          const float2 c1 = angle_cs(j * rpos, s_invf[8 * p + 2 * e2 + 1]);
+          cs = make_float4(c0.x, c0.y, c1.x, c1.y);
+        } else {
+          cs = trow[e2];
+        }
         rot_neg(bf16_at(a, 2 * e2), bf16_at(c, 2 * e2), cs.x, cs.y, y1[2 * e2], y2[2 * e2]);
         rot_neg(bf16_at(a, 2 * e2 + 1), bf16_at(c, 2 * e2 + 1), cs.z, cs.w, y1[2 * e2 + 1],
                 y2[2 * e2 + 1]);
@@ -207,7 +221,8 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
       if (jc < L) {
         const int m = args.sel[g * kSelPairs + cp];
         const uint16_t* row = Kp + ((size_t)(start + jc) * Hkv + g) * D;
-        const float2 cs = tab[(size_t)(jc - alias_fast(jc, gdiv)) * 64 + m];
+        const float2 cs = interp ? angle_cs(jc * rpos, s_invf[m])
+                                 : tab[(size_t)(jc - alias_fast(jc, gdiv)) * 64 + m];
         float z1, z2;
         rot_neg(__uint_as_float((uint32_t)row[m] << 16), __uint_as_float((uint32_t)row[m + 64] << 16),
                 cs.x, cs.y, z1, z2);
@@ -302,6 +317,14 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const uint16_t* __restrict__ Qp = (const uint16_t*)args.Q;
   const uint16_t* __restrict__ Kp = (const uint16_t*)args.K;
   const float2* __restrict__ tab = args.tab;
+  // continuous remote positions: n(x) = x - x/G, angles evaluated here (theta_m in LDS)
+  const bool interp = args.interp != 0;
+  const double rpos = (double)(G - 1) / (double)G;
+  __shared__ double s_invf[D / 2];
+  if (interp) {
+    if (tid < D / 2) s_invf[tid] = inv_freq64(args.theta, tid, D);
+    __syncthreads();  // no transfer is in flight yet
+  }
 
   // ---- this wave's 32-query block -------------------------------------------------
   const int qhead = g * REP + wave / PBLK;
@@ -354,7 +377,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       float y1[8], y2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float2 cs = trow[16 * s + 8 * hf + e];
+        const float2 cs = interp ? angle_cs(qrow_i * rpos, s_invf[16 * s + 8 * hf + e])
+                                 : trow[16 * s + 8 * hf + e];
         rot_neg(bf16_at(raw[s], e), bf16_at(raw[s + 4], e), cs.x, cs.y, y1[e], y2[e]);
       }
       qop[s] = u32x4{pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
@@ -368,7 +392,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       const int m = args.sel[g * kSelPairs + p];
       const float x1 = __uint_as_float((uint32_t)qrow[m] << 16);
       const float x2 = __uint_as_float((uint32_t)qrow[m + 64] << 16);
-      const float2 cs = trow[m];
+      const float2 cs = interp ? angle_cs(qrow_i * rpos, s_invf[m]) : trow[m];
       float y1, y2;
       rot_neg(x1, x2, cs.x, cs.y, y1, y2);
       uint32_t h1, l1, h2, l2;

@@ -55,6 +55,18 @@ typedef enum { BF_F32 = 0, BF_BF16 = 1 } bf_dtype;
 
 typedef enum { BF_OP_ROPE = 0, BF_OP_PREFILL = 1, BF_OP_DECODE = 2, BF_OP_PREFILL_IE = 3 } bf_op;
 
+/*
+ * Attention variants (bifocal_prefill_variant, bifocal_decode_variant):
+ *   BF_VARIANT_BIFOCAL  the method: remote pairs at f(x) = floor(x / G).
+ *   BF_VARIANT_INTERP   remote pairs at the continuous positions x / G: frequency
+ *                       interpolation, the alternative the pages' ablation compares
+ *                       aliasing against ("aliasing vs interpolation").
+ *   BF_VARIANT_WINDOW   the local window alone (0 <= i - j < w0, standard RoPE), the
+ *                       shape of a sliding-window layer in the hybrid models the pages
+ *                       discuss (Jet-Nemotron); remote pairs are dropped.
+ */
+typedef enum { BF_VARIANT_BIFOCAL = 0, BF_VARIANT_INTERP = 1, BF_VARIANT_WINDOW = 2 } bf_variant;
+
 /* HIP stream handle; 0 is the default stream. */
 typedef struct ihipStream_t* bf_stream;
 
@@ -105,6 +117,20 @@ bf_status bifocal_prefill(const void* Q, const void* K, const void* V, void* O, 
                           int32_t D, int32_t w0, int32_t w_pretrained, double theta,
                           float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
                           bf_stream stream);
+
+/*
+ * bifocal_prefill_variant -- bifocal_prefill for an attention variant (bf_variant).
+ *   BF_VARIANT_BIFOCAL is bifocal_prefill.  BF_VARIANT_INTERP and BF_VARIANT_WINDOW run
+ *   the bf16 matrix-core path only (dt = BF_BF16, D = 128, else BF_EUNSUPPORTED); the
+ *   continuous remote angles are evaluated in float64 in the kernels (one rounding to
+ *   float32, like table entries).  Arguments, layouts, workspace and errors as for
+ *   bifocal_prefill; BF_EINVAL for an unknown variant.
+ */
+bf_status bifocal_prefill_variant(const void* Q, const void* K, const void* V, void* O, float* lse,
+                                  const int32_t* cu_seqlens, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t D, int32_t w0, int32_t w_pretrained, double theta,
+                                  float softmax_scale, int32_t variant, bf_dtype dt, void* ws,
+                                  size_t ws_bytes, bf_stream stream);
 
 /*
  * bifocal_prefill_ie -- the same attention as bifocal_prefill, computed literally as
@@ -181,6 +207,19 @@ bf_status bifocal_decode_batch(const void* q, const void* Kcache, const void* Vc
                                int32_t Hkv, int32_t D, int32_t w0, int32_t w_pretrained,
                                double theta, float softmax_scale, bf_dtype dt, void* ws,
                                size_t ws_bytes, bf_stream stream);
+
+/*
+ * bifocal_decode_variant -- bifocal_decode_batch for an attention variant (bf_variant).
+ *   BF_VARIANT_BIFOCAL is bifocal_decode_batch.  The other variants need dt = BF_BF16 and
+ *   D = 128 (BF_EUNSUPPORTED otherwise); BF_VARIANT_WINDOW reads only the last w0 cache
+ *   rows of each sequence.  Arguments, layouts, workspace and errors as for
+ *   bifocal_decode_batch; BF_EINVAL for an unknown variant.
+ */
+bf_status bifocal_decode_variant(const void* q, const void* Kcache, const void* Vcache, void* o,
+                                 float* lse, const int32_t* pos, int32_t B, int32_t S, int32_t Hq,
+                                 int32_t Hkv, int32_t D, int32_t w0, int32_t w_pretrained,
+                                 double theta, float softmax_scale, int32_t variant, bf_dtype dt,
+                                 void* ws, size_t ws_bytes, bf_stream stream);
 
 /*
  * bifocal_workspace_bytes -- workspace size for an operation.

@@ -31,7 +31,7 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("bifocal_prefill", "bifocal_decode", "rope_apply", "bifocal_workspace_bytes",
               "bifocal_status_string", "bifocal_group_size", "bifocal_prefill_ie",
-              "bifocal_decode_batch"):
+              "bifocal_decode_batch", "bifocal_prefill_variant", "bifocal_decode_variant"):
         assert n in names
 
 
@@ -187,6 +187,25 @@ def test_decode_workspace_grows_with_batch(lib):
     many = lib.bifocal_workspace_bytes(2, 4096, 0, 16, 32, 8, 128)
     assert many >= 16 * 32 * 128 * 130 * 4 > one
     assert lib.bifocal_workspace_bytes(2, 4096, 0, -1, 32, 8, 128) == 0
+
+
+def test_variants_reject_bad_arguments_before_launch(lib):
+    def pre(variant, dt=1, D=128):
+        arr = (ctypes.c_int32 * 2)(0, 64)
+        return lib.bifocal_prefill_variant(16, 16, 16, 16, 0, ctypes.cast(arr, ctypes.c_void_p),
+                                           1, 4, 1, D, 4, 16, 1e4, 0.0, variant, dt, 256, 1 << 30,
+                                           None)
+
+    def dec(variant, dt=1, D=128):
+        arr = (ctypes.c_int32 * 2)(100, 7)
+        return lib.bifocal_decode_variant(16, 16, 16, 16, 0, ctypes.cast(arr, ctypes.c_void_p), 2,
+                                          512, 4, 1, D, 4, 16, 1e4, 0.0, variant, dt, 256,
+                                          1 << 12, None)
+    assert pre(3) == BF_EINVAL and pre(-1) == BF_EINVAL
+    assert pre(1, dt=0) == BF_EUNSUPPORTED and pre(2, dt=0) == BF_EUNSUPPORTED
+    assert dec(7) == BF_EINVAL
+    assert dec(1, dt=0) == BF_EUNSUPPORTED and dec(2, D=64) == BF_EUNSUPPORTED
+    assert dec(1) == BF_EWORKSPACE   # valid variant, workspace too small
 
 
 def test_rope_apply_rejects_bad_arguments(lib):

@@ -372,3 +372,71 @@ def test_prefill_ie_matches_oracle_and_fused(bf, case):
         # (relative 2^-8 at worst), which the merge scales by the conditioning
         assert np.all(d_l <= BF16_TOL["lse_abs"] + 2.0 ** -7 * cond)
         assert np.all(d_o <= BF16_TOL["max_abs"] + 2.0 ** -7 * cond * vmax)
+
+
+# ---------------------------------------------------------------------------
+# variants: continuous remote positions and window-only layers
+# ---------------------------------------------------------------------------
+
+VARIANT_CASES = [
+    # name, Hq, Hkv, seqlens, w_pretrained, w0, outliers
+    ("v_rep4_g4", 8, 2, (1000,), 256, 100, 4),
+    ("v_rep2_ragged", 8, 4, (513, 64, 1), 128, 200, 4),
+    ("v_rep8_g3", 16, 2, (777,), 300, 50, 0),
+    ("v_rep1_g1", 4, 4, (300,), 512, 64, 0),
+]
+
+
+@pytest.mark.parametrize("variant", ["interp", "window"])
+@pytest.mark.parametrize("case", VARIANT_CASES, ids=[c[0] for c in VARIANT_CASES])
+def test_prefill_variant_matches_oracle(bf, variant, case):
+    name, Hq, Hkv, seqlens, w_pre, w0, outl = case
+    w = W.Workload(name, "prefill", "bf16", Hq=Hq, Hkv=Hkv, D=128, w0=w0, w_pretrained=w_pre,
+                   theta=1e6, seqlens=seqlens, outliers=outl, seed=600 + len(name))
+    say("prefill", variant, w)
+    Q, K, V, cu = prefill_inputs(w)
+    O, lse = bf.bifocal_prefill_variant(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"),
+                                        [int(c) for c in cu], w.w0, w.w_pretrained, w.theta,
+                                        variant=variant)
+    torch.cuda.synchronize()
+    Og, Lg = host(O), lse.cpu().numpy()
+    for b, (rows, Or, Lr) in enumerate(bifocal_prefill_ref(Q, K, V, cu, w.w0, w.w_pretrained,
+                                                           w.theta, variant=variant)):
+        if Or is None:
+            continue
+        s0 = int(cu[b])
+        e = errors(Og[s0 + rows], Or, Lg[:, s0 + rows].T, Lr)
+        say(f"  seq {b}: G={group_size(int(cu[b + 1] - cu[b]), w.w_pretrained)} {e}")
+        assert within(e, BF16_TOL), (b, e)
+
+
+def test_prefill_interp_g1_equals_method_bitwise(bf):
+    w = W.Workload("g1i", "prefill", "bf16", Hq=8, Hkv=2, D=128, w0=40, w_pretrained=4096,
+                   theta=1e6, seqlens=(900,), seed=41)
+    Q, K, V, cu = prefill_inputs(w)
+    args = (dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), [int(c) for c in cu], w.w0,
+            w.w_pretrained, w.theta)
+    O1, L1 = bf.bifocal_prefill(*args)
+    O2, L2 = bf.bifocal_prefill_variant(*args, variant="interp")
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+@pytest.mark.parametrize("variant", ["interp", "window"])
+def test_decode_variant_matches_oracle(bf, variant):
+    w = W.Workload("decv", "decode", "bf16", Hq=16, Hkv=4, D=128, w0=100, w_pretrained=700,
+                   theta=1e6, cache_len=3000, decode_steps=1, outliers=4, seed=81)
+    positions = [2999, 1400, 699, 700, 99, 0, 2048]
+    q_raw, Kc, Vc = _batch_caches(w, len(positions), 3000)
+    q = np.stack([std_query(q_raw[b], positions[b], w.theta, "bf16")
+                  for b in range(len(positions))])
+    o, lse = bf.bifocal_decode_variant(dev(q, "bf16"), dev(Kc, "bf16"), dev(Vc, "bf16"),
+                                       positions, w.w0, w.w_pretrained, w.theta, variant=variant)
+    torch.cuda.synchronize()
+    og, lg = host(o), lse.cpu().numpy()
+    for b, pos in enumerate(positions):
+        Or, Lr = bifocal_decode_ref(q[b], Kc[b], Vc[b], pos, w.w0, w.w_pretrained, w.theta,
+                                    variant=variant)
+        e = errors(og[b], Or, lg[b], Lr)
+        say(f"  {variant} seq {b} pos={pos} G={group_size(pos + 1, w.w_pretrained)} {e}")
+        assert within(e, BF16_TOL), (variant, pos, e)

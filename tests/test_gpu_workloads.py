@@ -34,13 +34,17 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
 
 
-def _prefill_case(bf, name, n_uniform, ie=False):
+def _prefill_case(bf, name, n_uniform, ie=False, variant="bifocal"):
     w = W.get(name)
     say(f"{name}: building inputs on the CPU")
     Q, K, V, cu = prefill_inputs(w)
-    say(f"{name}: GPU prefill" + (" (three-pass inclusion-exclusion form)" if ie else ""))
-    fn = bf.bifocal_prefill_ie if ie else bf.bifocal_prefill
-    O, lse = fn(dev(Q), dev(K), dev(V), [int(c) for c in cu], w.w0, w.w_pretrained, w.theta)
+    say(f"{name}: GPU prefill" + (" (three-pass inclusion-exclusion form)" if ie else "")
+        + (f" (variant {variant})" if variant != "bifocal" else ""))
+    args = (dev(Q), dev(K), dev(V), [int(c) for c in cu], w.w0, w.w_pretrained, w.theta)
+    if variant != "bifocal":
+        O, lse = bf.bifocal_prefill_variant(*args, variant=variant)
+    else:
+        O, lse = (bf.bifocal_prefill_ie if ie else bf.bifocal_prefill)(*args)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(O).all())
     for b in range(len(cu) - 1):
@@ -52,7 +56,8 @@ def _prefill_case(bf, name, n_uniform, ie=False):
         Og = O[s + rows].float().cpu().numpy()
         Lg = lse[:, s + rows].T.cpu().numpy()
         say(f"{name}: oracle on {len(rows)} rows x {w.Hq} heads of sequence {b} (L={L}, G={G})")
-        Or, Lr = bifocal_rows(Q[s:e], K[s:e], V[s:e], rows, w.w0, w.w_pretrained, w.theta)
+        Or, Lr = bifocal_rows(Q[s:e], K[s:e], V[s:e], rows, w.w0, w.w_pretrained, w.theta,
+                              variant=variant)
         if not ie:
             err = errors(Og, Or, Lg, Lr)
             say(f"{name}: seq {b} {err}")
@@ -85,6 +90,11 @@ def test_qwen3_4b_128k(bf):
 
 def test_qwen3_8b_ragged(bf):
     _prefill_case(bf, "qwen3_8b_ragged", 16)
+
+
+def test_qwen3_4b_128k_interp_variant(bf):
+    # continuous remote positions x / G at full size (angles evaluated in the kernels)
+    _prefill_case(bf, "qwen3_4b_128k", 8, variant="interp")
 
 
 def test_qwen3_4b_128k_three_pass(bf):
