@@ -9,26 +9,34 @@
 // online softmax, with no mask matrix: tiles are classified from indices alone.
 //
 // Design for CDNA4 (one workgroup = one KV head x a block of query positions for all
-// Hq/Hkv query heads of the group; 8 waves, each wave 32 query rows):
+// Hq/Hkv query heads of the group; 8 waves, each wave 32 query rows, two per SIMD):
 //   * S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_32x32x16: the query is the MFMA
 //     column, so every query row lives in one lane pair (l, l^32) and P goes from
 //     the score accumulator to the PV operand without a trip through LDS.
-//   * K/V tiles of 64 keys are staged through LDS (double-buffered, one barrier per
-//     tile) and shared by all query heads of the group.  V is stored transposed so
-//     that the PV operand is two 8-byte LDS reads.
-//   * Tiles are classified from indices: REMOTE (every pair outside the window) take
-//     the remote-only path, LOCAL (every pair inside) the standard path, and the few
-//     STRADDLE tiles compute both score sets and select per element.
+//   * A key-preparation pass writes, once per call, a record per (KV head, 32-key
+//     tile): the keys rotated to their remote positions (fp16), the hi/lo operand of
+//     the selected pairs, and V transposed.  The main kernel copies records (remote
+//     tiles) or K rows (local tiles) into an eight-slot LDS ring with LDS-DMA, six
+//     tiles ahead, shared by all query heads of the group; the waves meet at a barrier
+//     after every second tile.
+//   * Tiles are classified from indices: the workgroup walks a remote pass (tiles with
+//     remote pairs) and a local pass (tiles with window pairs); the few tiles that
+//     straddle the window edge are visited by both passes, each masking the other
+//     class, so every pair is scored once by its own rule.
 //   * Local scores use the exact bf16 input bytes (bf16 MFMA), so G = 1 reproduces
 //     plain causal attention.  Remote scores need the correction rotation R(f(x) - x)
 //     (section 2, rotations compose additively), applied in fp32 registers once per
-//     key tile for the whole group and once per query row; the rotated operands are
+//     key and call (key preparation) and once per query row; the rotated operands are
 //     rounded to fp16 (same MFMA rate as bf16 on gfx950, 3 more mantissa bits), and
 //     for the 4 RoPE pairs per KV head with the largest |q||k| bound a hi/lo split adds
 //     one K=16 MFMA step (hi*lo + lo*hi) so that outlier channels do not lose the
 //     low-order bits of their products.
 //   * Online softmax in the base-2 domain with a lazy running max (rescale only when
 //     the max grows by more than 8), row sums kept per lane half.
+//   * The same kernel also runs the three passes of the pages' inclusion-exclusion
+//     form (mode 1: remote over all causal pairs, 2: remote over the window, 3: local
+//     over the window) and the continuous-position variant (remote angles x/G - x
+//     evaluated in float64 instead of read from the table).
 #include <type_traits>
 
 #include "bf_common.h"
