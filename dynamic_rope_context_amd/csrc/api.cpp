@@ -5,8 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
-#include <chrono>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -21,7 +19,7 @@ extern "C" {
 
 namespace bifocal {
 hipError_t launch_table_ensure(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
-                               bool full, uint32_t token, hipStream_t stream);
+                               bool full, hipStream_t stream);
 hipError_t launch_rope_apply(void* x, const int32_t* pos, int pos0, int T_, int H, int D,
                              double theta, int G, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& args, hipStream_t stream);
@@ -60,14 +58,6 @@ struct TableHint {
 };
 std::mutex g_hint_mu;
 std::vector<TableHint> g_hints;
-std::atomic<uint32_t> g_token{0};
-
-uint32_t next_token() {
-  static const uint32_t seed = (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count();
-  uint32_t t = seed ^ (0x9e3779b9u * (g_token.fetch_add(1) + 1));
-  return t ? t : 1u;
-}
-
 bf_status ensure_table(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
                        hipStream_t stream) {
   bool believed = false;
@@ -76,7 +66,7 @@ bf_status ensure_table(void* ws, const WsLayout& lay, int D, double theta, int n
     for (auto& h : g_hints)
       if (h.ws == ws && h.theta == theta && h.D == D && h.n_valid >= n_needed) believed = true;
   }
-  hipError_t e = launch_table_ensure(ws, lay, D, theta, n_needed, !believed, next_token(), stream);
+  hipError_t e = launch_table_ensure(ws, lay, D, theta, n_needed, !believed, stream);
   if (e != hipSuccess) return BF_EHIP;
   if (!believed) {
     const long long want = ((long long)n_needed + 65535) / 65536 * 65536;

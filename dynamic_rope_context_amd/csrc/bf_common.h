@@ -30,8 +30,7 @@ struct TableHeader {
   double theta;
   int32_t D;
   int32_t n_valid;     // positions covered
-  uint64_t done;       // builder blocks finished, tagged with the build's token
-  uint32_t pad[56];
+  uint32_t pad[58];
 };
 static_assert(sizeof(TableHeader) == 256, "header is one 256-byte slot");
 

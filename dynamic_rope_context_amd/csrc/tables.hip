@@ -7,28 +7,27 @@
 // aliased position f(x) (Jet-Long technical summary, "Methodology" section 1 for f,
 // section 2 "on-the-fly correction rotation" for the additive composition).
 //
-// The table persists in the caller's workspace behind a header.  Every block reads
-// the header first and leaves at once when it already describes (theta, D) with
-// enough positions, so a launch on a valid table costs one header read per block.
-// When a build runs, the last block to finish publishes the header; blocks count
-// themselves with a token-tagged 64-bit counter so that stale workspace contents
-// can never be mistaken for a finished count.
+// The table persists in the caller's workspace behind a header.  A build is two
+// launches on the caller's stream: every block of the build kernel reads the header
+// first and leaves at once when it already describes (theta, D) with enough
+// positions; otherwise the blocks fill the rows.  A one-thread publish kernel then
+// writes the header (stream order makes every row of the build visible to it and to
+// later kernels).  No block waits for another and nothing is counted, so a build
+// costs its arithmetic only.
 #include "bf_common.h"
 
 namespace bifocal {
 
-__global__ void __launch_bounds__(256) table_ensure_kernel(TableHeader* hdr, float2* tab,
-                                                           int n_cap, int n_build, int n_needed,
-                                                           int D, double theta, uint32_t token) {
+__device__ __forceinline__ bool table_valid(const volatile TableHeader* h, int D, double theta,
+                                            int n_needed) {
+  return h->magic == kTableMagic && h->theta == theta && h->D == D && h->n_valid >= n_needed;
+}
+
+__global__ void __launch_bounds__(256) table_build_kernel(const TableHeader* hdr, float2* tab,
+                                                          int n_build, int n_needed, int D,
+                                                          double theta) {
   __shared__ int s_skip;
-  if (threadIdx.x == 0) {
-    volatile TableHeader* h = hdr;
-    const bool ok = h->magic == kTableMagic && h->theta == theta && h->D == D;
-    s_skip = ok && h->n_valid >= n_needed ? 1 : 0;
-    // Rows past this call's capacity may be overwritten by its scratch: forget them.
-    // (n_needed <= n_cap, so lowering n_valid to n_cap never changes a skip decision.)
-    if (ok && blockIdx.x == 0 && h->n_valid > n_cap) h->n_valid = n_cap;
-  }
+  if (threadIdx.x == 0) s_skip = table_valid(hdr, D, theta, n_needed) ? 1 : 0;
   __syncthreads();
   if (s_skip) return;
 
@@ -48,50 +47,46 @@ __global__ void __launch_bounds__(256) table_ensure_kernel(TableHeader* hdr, flo
     sincos_reduced(a, &s, &c);
     tab[idx] = make_float2((float)c, (float)s);
   }
+}
 
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long* cnt = reinterpret_cast<unsigned long long*>(&hdr->done);
-    unsigned long long old = *(volatile unsigned long long*)cnt, assumed, nv;
-    do {
-      assumed = old;
-      nv = ((assumed >> 32) == token) ? assumed + 1ull
-                                      : (((unsigned long long)token << 32) | 1ull);
-      old = atomicCAS(cnt, assumed, nv);
-    } while (old != assumed);
-    const unsigned count = (unsigned)(nv & 0xffffffffull);
-    if (count == gridDim.x) {
-      __threadfence();
-      volatile TableHeader* h = hdr;
-      h->magic = 0;
-      __threadfence();
-      h->theta = theta;
-      h->D = D;
-      h->n_valid = n_build;
-      __threadfence();
-      h->magic = kTableMagic;
-      __threadfence();
-    }
+__global__ void table_publish_kernel(TableHeader* hdr, int n_cap, int n_build, int n_needed,
+                                     int D, double theta) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  volatile TableHeader* h = hdr;
+  if (table_valid(h, D, theta, n_needed)) {
+    // Rows past this call's capacity may be overwritten by its scratch: forget them
+    // (n_needed <= n_cap, so this never turns the table invalid for this call).
+    if (h->n_valid > n_cap) h->n_valid = n_cap;
+    return;
   }
+  // the build kernel of this call filled rows 0 .. n_build-1
+  h->magic = 0;
+  h->theta = theta;
+  h->D = D;
+  h->n_valid = n_build;
+  h->magic = kTableMagic;
 }
 
 // Enqueue the table check/build.  `full` selects a grid that builds quickly; a
 // one-block launch still builds (slowly) if the header turns out to be stale.
 hipError_t launch_table_ensure(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
-                               bool full, uint32_t token, hipStream_t stream) {
+                               bool full, hipStream_t stream) {
   TableHeader* hdr = reinterpret_cast<TableHeader*>(ws);
   float2* tab = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + lay.table_off);
   // Build ahead of need (to the next multiple of 64K positions, within capacity) so
-  // that decode steps walking forward one position at a time rarely rebuild.
+  // that calls walking forward one position at a time rarely rebuild.
   const long long want = ((long long)n_needed + 65535) / 65536 * 65536;
   const int n_build = (int)(want < lay.n_cap ? want : lay.n_cap);
   size_t total = (size_t)n_build * (D / 2);
   int blocks = full ? (int)((total + 255) / 256) : 1;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(table_ensure_kernel, dim3(blocks), dim3(256), 0, stream, hdr, tab,
-                     lay.n_cap, n_build, n_needed, D, theta, token);
+  hipLaunchKernelGGL(table_build_kernel, dim3(blocks), dim3(256), 0, stream, hdr, tab, n_build,
+                     n_needed, D, theta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(table_publish_kernel, dim3(1), dim3(64), 0, stream, hdr, lay.n_cap, n_build,
+                     n_needed, D, theta);
   return hipGetLastError();
 }
 

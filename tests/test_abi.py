@@ -208,6 +208,13 @@ def test_variants_reject_bad_arguments_before_launch(lib):
     assert dec(1) == BF_EWORKSPACE   # valid variant, workspace too small
 
 
+def test_positions_beyond_the_alias_range_are_rejected(lib):
+    # floor(x / G) is evaluated by multiply-shift, exact below 2^24 positions
+    assert _prefill(lib, cu=[0, 1 << 24]) == BF_EUNSUPPORTED
+    assert _decode(lib, pos=(1 << 24) - 1) == BF_EUNSUPPORTED
+    assert _decode_batch(lib, pos=[5, (1 << 24) - 1], S=1 << 24) == BF_EUNSUPPORTED
+
+
 def test_rope_apply_rejects_bad_arguments(lib):
     f = lib.rope_apply
     assert f(16, None, 0, 10, 2, 7, 1e4, 1, 1, None) == BF_EINVAL     # odd D
