@@ -92,6 +92,28 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise BifocalError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
 
 
+def _outputs(ref: torch.Tensor, out, lse, want_lse: bool, lse_shape):
+    """Allocate or check the output tensors: out like ``ref``, lse float32 of lse_shape on
+    the same device.  A caller-provided buffer of the wrong shape, dtype or device is an
+    error (the library writes through raw pointers)."""
+    if out is None:
+        out = torch.empty_like(ref)
+    elif out.shape != ref.shape or out.dtype != ref.dtype or out.device != ref.device:
+        raise BifocalError(f"out must be {tuple(ref.shape)} {ref.dtype} on {ref.device}")
+    if lse is None and want_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=ref.device)
+    elif lse is not None and (tuple(lse.shape) != tuple(lse_shape) or lse.dtype != torch.float32
+                              or lse.device != ref.device):
+        raise BifocalError(f"lse must be {tuple(lse_shape)} float32 on {ref.device}")
+    return out, lse
+
+
+def _same(ref: torch.Tensor, *ts) -> None:
+    for t in ts:
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise BifocalError("inputs must share one dtype and one device")
+
+
 def _dev(t: torch.Tensor, name: str) -> int:
     if not t.is_cuda:
         raise BifocalError(f"{name} must be a device tensor")
@@ -166,10 +188,8 @@ def _prefill(fn, op, Q, K, V, cu_seqlens, w0, w_pretrained, theta, softmax_scale
     cu = [int(c) for c in cu_seqlens]
     B = len(cu) - 1
     cu_arr = (ctypes.c_int32 * len(cu))(*cu)
-    if out is None:
-        out = torch.empty_like(Q)
-    if lse is None and want_lse:
-        lse = torch.empty((Hq, T), dtype=torch.float32, device=Q.device)
+    _same(Q, K, V)
+    out, lse = _outputs(Q, out, lse, want_lse, (Hq, T))
     if workspace is None:
         max_len = max([cu[b + 1] - cu[b] for b in range(B)] + [0])
         workspace = Workspace.for_op(op, max(max_len, 1), Hq, Hkv, D, Q.device,
@@ -222,10 +242,8 @@ def bifocal_decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, 
     S, Hkv = Kcache.shape[0], Kcache.shape[1]
     if pos + 1 > S:
         raise BifocalError("the cache holds fewer than pos + 1 entries")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    _same(q, Kcache, Vcache)
+    out, lse = _outputs(q, out, lse, want_lse, (Hq,))
     if workspace is None:
         workspace = Workspace.for_op(OP_DECODE, pos + 1, Hq, Hkv, D, q.device)
     _check(lib().bifocal_decode(
@@ -252,10 +270,8 @@ def bifocal_decode_batch(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Te
     pl = [int(p) for p in pos]
     if len(pl) != B or Kcache.shape[0] != B or Kcache.shape[3] != D:
         raise BifocalError("q, caches and pos disagree on the batch")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _same(q, Kcache, Vcache)
+    out, lse = _outputs(q, out, lse, want_lse, (B, Hq))
     if workspace is None:
         workspace = Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
                                      num_seqs=max(B, 1))
@@ -307,10 +323,8 @@ def bifocal_decode_variant(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.
     pl = [int(p) for p in pos]
     if len(pl) != B or Kcache.shape[0] != B or Kcache.shape[3] != D:
         raise BifocalError("q, caches and pos disagree on the batch")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _same(q, Kcache, Vcache)
+    out, lse = _outputs(q, out, lse, want_lse, (B, Hq))
     if workspace is None:
         workspace = Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
                                      num_seqs=max(B, 1))

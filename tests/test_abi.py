@@ -232,3 +232,25 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(b, "_lib_handle", None)
     with pytest.raises(ImportError):
         b.lib()
+
+
+def test_binding_checks_caller_buffers_before_any_call():
+    # wrong output shapes or dtypes are rejected before a pointer reaches the library
+    import torch
+    import dynamic_rope_context_amd as b
+    Q = torch.zeros(8, 4, 128, dtype=torch.bfloat16)
+    K = torch.zeros(8, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(b.BifocalError):
+        b.bifocal_prefill(Q, K, K, [0, 8], 4, 16, 1e4, out=torch.zeros(8, 4, 64, dtype=torch.bfloat16))
+    with pytest.raises(b.BifocalError):
+        b.bifocal_prefill(Q, K, K, [0, 8], 4, 16, 1e4, lse=torch.zeros(8, 4))
+    with pytest.raises(b.BifocalError):
+        b.bifocal_prefill(Q, K.float(), K, [0, 8], 4, 16, 1e4)
+    q = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(b.BifocalError):
+        b.bifocal_decode(q, K, K, 5, 4, 16, 1e4, out=torch.zeros(4, 128))
+    with pytest.raises(b.BifocalError):
+        b.bifocal_decode_batch(q[None], K[None], K[None], [5], 4, 16, 1e4,
+                               lse=torch.zeros(2, 4))
+    with pytest.raises(b.BifocalError):
+        b.bifocal_decode_variant(q[None], K[None], K[None], [5], 4, 16, 1e4, variant="yarn")
