@@ -75,10 +75,7 @@ constexpr int NSTAGE = 8;          // LDS ring of virtual tiles
 // Tiles issued ahead of the one being computed.  The workgroup meets at a barrier
 // after every second tile, so a slot is refilled two tiles after its last use.
 constexpr int PREF = NSTAGE - 2;
-// after the ring: each wave's hi/lo query operand of the remote pass (one 16-byte
-// chunk per lane), read back per tile instead of held in registers
-constexpr size_t kQcorOff = NSTAGE * sizeof(Stage);
-constexpr size_t kSmem = kQcorOff + NW * 64 * 16;
+constexpr size_t kSmem = NSTAGE * sizeof(Stage);
 
 }  // namespace mf
 
@@ -368,8 +365,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // ---- query operands -------------------------------------------------------------
   // B operand of S^T = K Q^T: lane (column ln, half hf) holds channels 16s + 8hf + e.
   u32x4 qop[8];   // remote pass: fp16 of R(f(i)-i) q; local pass: bf16 q
-  // hi (half 0) or lo (half 1) of the 8 selected remote channels, kept in LDS
-  u32x4* const qcor_lds = reinterpret_cast<u32x4*>(smem_raw + kQcorOff) + 64 * wave + lane;
+  u32x4 qcor;     // hi (half 0) or lo (half 1) of the 8 selected remote channels
   auto load_q_std = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
@@ -409,8 +405,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       part[p] = hf ? l1 : h1;
       part[p + 4] = hf ? l2 : h2;
     }
-    *qcor_lds = u32x4{part[0] | (part[1] << 16), part[2] | (part[3] << 16),
-                      part[4] | (part[5] << 16), part[6] | (part[7] << 16)};
+    qcor = u32x4{part[0] | (part[1] << 16), part[2] | (part[3] << 16),
+                 part[4] | (part[5] << 16), part[6] | (part[7] << 16)};
   };
 
   // ---- staging: LDS-DMA straight from the key-tile records / K rows ----------------
@@ -477,7 +473,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     for (int s = 0; s < 8; ++s)
       sacc = mfma_f16(*reinterpret_cast<const u32x4*>(krow + 16 * s), qop[s], sacc);
     const uint16_t* crow = st.kc + ln * KC_LD + 8 * (hf ^ ((ln >> 3) & 1));
-    return mfma_f16(*reinterpret_cast<const u32x4*>(crow), *qcor_lds, sacc);
+    return mfma_f16(*reinterpret_cast<const u32x4*>(crow), qcor, sacc);
   };
   auto qk_local = [&](int so) __attribute__((always_inline)) -> f32x16 {
     const Stage& st = *reinterpret_cast<const Stage*>(smem_raw + so);
