@@ -150,14 +150,20 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   };
   auto load_blk = [&](int i, Blk& x) __attribute__((always_inline)) {
     const int j0 = jb + (w + i * nsplit) * BK;
+    // 64-bit offset of the block (uniform), 32-bit offsets of the lanes within it.  A
+    // wave without blocks still loads one (the static wait counts): its j0 lies past
+    // pos, so the base is clamped to pos too and every lane offset stays in [0, 15].
+    const int jbase = min(j0, pos);
+    const uint16_t* kb = kg + (size_t)jbase * rs;
+    const uint16_t* vb = vg + (size_t)jbase * rs;
     const int jk = min(j0 + l16, pos);
-    const uint16_t* kr = kg + (uint32_t)jk * rs + 8 * kq;
+    const uint16_t* kr = kb + (uint32_t)(jk - jbase) * rs + 8 * kq;
 #pragma unroll
     for (int s = 0; s < 4; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const int jv = min(j0 + 2 * kp + k2, pos);
-      const uint16_t* vr = vg + (uint32_t)jv * rs + 16 * cg;
+      const uint16_t* vr = vb + (uint32_t)(jv - jbase) * rs + 16 * cg;
 #pragma unroll
       for (int c = 0; c < 2; ++c) x.v[k2][c] = *reinterpret_cast<const uint4*>(vr + 8 * c);
     }
