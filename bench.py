@@ -12,6 +12,8 @@ Prints one JSON line on stdout; progress goes to stderr.
              set over the local window: F = 4*D*Hq*sum_i(i+1) + 2*D*Hq*sum_i min(i+1, w0)
   roofline   the prefill kernel against the dense bf16 MFMA peak (2500 TFLOP/s)
   decode     KV GB/s = bytes of K and V read per step / step time, against 8000 GB/s
+  decode_batch  a batch of 8 sequences of 16K rows each in one bifocal_decode_batch call
+             per step (the same K + V bytes per step as the 128K sequence)
   three_pass the literal inclusion-exclusion form of the same prefill (local/window,
              remote/causal and remote/window passes merged by their LSEs): time and the
              ratio to the fused call
@@ -176,6 +178,45 @@ def bench_decode(bf, torch, W, passes, warmup, w0=None):
     return w, ms_step, kv_bytes
 
 
+def bench_decode_batch(bf, torch, W, passes, warmup, B=8, S=16384):
+    """Batched decode: B sequences of the decode layer's shape, each at position S - 1 of
+    its own S-row cache (the same K + V bytes per step as one 128K sequence)."""
+    w = W.get("qwen3_8b_decode_128k")
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 7)
+    k = torch.randn((B, S, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, S, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, w.Hq, w.D), generator=g, device="cuda").to(torch.bfloat16)
+    for b in range(B):
+        bf.rope_apply(k[b], w.theta)
+    # each query at its sequence's position S - 1
+    bf.rope_apply(q, w.theta, pos=torch.full((B,), S - 1, dtype=torch.int32, device="cuda"))
+    positions = [S - 1] * B
+    ws = bf.Workspace.for_op(bf.OP_DECODE, S, w.Hq, w.Hkv, w.D, num_seqs=B)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, w.Hq), dtype=torch.float32, device="cuda")
+    steps = 64
+
+    def one_pass():
+        for _ in range(steps):
+            bf.bifocal_decode_batch(q, k, v, positions, w.w0, w.w_pretrained, w.theta, out=o,
+                                    lse=lse, workspace=ws)
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(passes):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (passes * steps) * 1e3
+    kv = 2.0 * B * S * w.Hkv * w.D * 2
+    return {"batch": B, "cache_rows_each": S, "us_per_step": round(us, 2),
+            "kv_GBps": round(kv / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(kv / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(W, F, n_uniform=200):
     """The oracle as it stands, on sampled query rows of the 128K workload (all 32
     heads), extrapolated to the whole prefill by the number of causal pairs."""
@@ -278,6 +319,9 @@ def main():
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": hbm_traffic("decode")}}
+        log("decode batch: 8 sequences x 16K rows per call")
+        dec["batch"] = bench_decode_batch(bf, torch, W, args.decode_passes, args.decode_warmup)
+        log(f"decode batch: {dec['batch']['us_per_step']} us/step, {dec['batch']['kv_GBps']} GB/s")
         if "metric" in result:
             result["decode"] = dec
         else:
@@ -287,7 +331,7 @@ def main():
                            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                            "dtype": "bf16", "data": "synthetic",
                            "config": {"workload": "qwen3_8b_decode_128k"},
-                           "roofline": dec["roofline"]})
+                           "roofline": dec["roofline"], "decode_batch": dec["batch"]})
     if not args.no_three_pass and args.only in ("all", "prefill"):
         log("three-pass prefill: qwen3_4b_128k, passes A, B, C + merge")
         _, tms, _, _ = bench_prefill(bf, torch, W, args.steps, args.warmup, three_pass=True)
