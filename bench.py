@@ -269,6 +269,8 @@ def main():
                     help="skip the vanilla-mode (w0 >= L) comparison runs")
     ap.add_argument("--no-three-pass", action="store_true",
                     help="skip the three-pass inclusion-exclusion comparison run")
+    ap.add_argument("--no-decode-batch", action="store_true",
+                    help="skip the batched decode run (8 sequences x 16K rows)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -319,9 +321,12 @@ def main():
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": hbm_traffic("decode")}}
-        log("decode batch: 8 sequences x 16K rows per call")
-        dec["batch"] = bench_decode_batch(bf, torch, W, args.decode_passes, args.decode_warmup)
-        log(f"decode batch: {dec['batch']['us_per_step']} us/step, {dec['batch']['kv_GBps']} GB/s")
+        if not args.no_decode_batch:
+            log("decode batch: 8 sequences x 16K rows per call")
+            dec["batch"] = bench_decode_batch(bf, torch, W, args.decode_passes,
+                                              args.decode_warmup)
+            log(f"decode batch: {dec['batch']['us_per_step']} us/step, "
+                f"{dec['batch']['kv_GBps']} GB/s")
         if "metric" in result:
             result["decode"] = dec
         else:
@@ -331,7 +336,7 @@ def main():
                            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                            "dtype": "bf16", "data": "synthetic",
                            "config": {"workload": "qwen3_8b_decode_128k"},
-                           "roofline": dec["roofline"], "decode_batch": dec["batch"]})
+                           "roofline": dec["roofline"], "decode_batch": dec.get("batch")})
     if not args.no_three_pass and args.only in ("all", "prefill"):
         log("three-pass prefill: qwen3_4b_128k, passes A, B, C + merge")
         _, tms, _, _ = bench_prefill(bf, torch, W, args.steps, args.warmup, three_pass=True)
