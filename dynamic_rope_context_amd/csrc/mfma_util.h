@@ -26,6 +26,14 @@ __device__ __forceinline__ void split_f16(float y, uint32_t& hi, uint32_t& lo) {
   lo = f16_bits_of(y - hf);
 }
 
+// max(x[l], x[l ^ 32]) in every lane l: the two 32-lane halves of a wave exchanged with
+// v_permlane32_swap (no LDS round trip, no wait on the wave's outstanding LDS reads).
+__device__ __forceinline__ float max_lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -502,7 +502,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     float mx = sacc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_lane_xor32(mx);
     const float cand = fmaxf(m_run, mx * c2);
     const bool need = cand > m_run + kLazy;
     if (__ballot(need)) {
@@ -567,9 +567,11 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       __attribute__((always_inline)) {
     constexpr bool QKREM = decltype(qkrem_c)::value;  // class of tile v+1's scores
     issue(v + PREF, slot(v + PREF));
-    s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
+    // Tile v's row max and rescale first, so that tile v+1's score MFMAs and tile v's
+    // exponentials (independent of each other) share one basic block and interleave.
     f32x16 sc = s_in;
     softmax_prep(v, sc, mk_c);
+    s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
     uint32_t pk[8];
     softmax_exp(sc, pk);
     pv(pk, slot(v));
