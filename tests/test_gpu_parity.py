@@ -242,7 +242,8 @@ def _batch_caches(w, B, S):
 
 
 @pytest.mark.parametrize("dt,D,Hq,Hkv", [("bf16", 128, 32, 8), ("bf16", 128, 8, 1),
-                                         ("f32", 128, 4, 4), ("bf16", 64, 8, 2)])
+                                         ("f32", 128, 4, 4), ("bf16", 64, 8, 2),
+                                         ("bf16", 128, 32, 16), ("bf16", 128, 24, 12)])
 def test_decode_batch_matches_oracle(bf, dt, D, Hq, Hkv):
     # ragged positions: G = 1, 1, 2, 3, 3 at w_pretrained 1000; window edges and a
     # one-key cache
