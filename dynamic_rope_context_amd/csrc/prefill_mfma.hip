@@ -108,33 +108,32 @@ __global__ void __launch_bounds__(256) pair_max_kernel(const uint16_t* __restric
 }
 
 // Top kSelPairs pairs per KV head by the bound max|k_m| * max_h |q_{h,m}| (squared).
-__global__ void pair_select_kernel(const uint32_t* __restrict__ mxq,
-                                   const uint32_t* __restrict__ mxk, int Hq, int Hkv,
-                                   int32_t* __restrict__ sel) {
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= Hkv) return;
+__global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restrict__ mxq,
+                                                         const uint32_t* __restrict__ mxk,
+                                                         int Hq, int Hkv,
+                                                         int32_t* __restrict__ sel) {
+  // one wave per KV head, lane = RoPE pair; kSelPairs rounds of a wave-wide argmax
+  // (the lowest pair wins a tie), each taking its winner out of the next rounds
+  const int g = blockIdx.x, m = threadIdx.x;
   const int rep = Hq / Hkv;
-  float bound[64];
-  for (int m = 0; m < 64; ++m) {
-    float q = 0.f;
-    for (int r = 0; r < rep; ++r) q = fmaxf(q, __uint_as_float(mxq[(g * rep + r) * 64 + m]));
-    bound[m] = q * __uint_as_float(mxk[g * 64 + m]);
-  }
-  int chosen[kSelPairs];
+  float q = 0.f;
+  for (int r = 0; r < rep; ++r) q = fmaxf(q, __uint_as_float(mxq[(g * rep + r) * 64 + m]));
+  float bound = q * __uint_as_float(mxk[g * 64 + m]);  // >= 0
   for (int p = 0; p < kSelPairs; ++p) {
-    int best = -1;
-    float bv = -1.f;
-    for (int m = 0; m < 64; ++m) {
-      bool used = false;
-      for (int q = 0; q < p; ++q) used |= chosen[q] == m;
-      if (!used && bound[m] > bv) {
-        bv = bound[m];
-        best = m;
+    float bv = bound;
+    int bi = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
       }
     }
-    chosen[p] = best;
+    if (m == 0) sel[g * kSelPairs + p] = bi;
+    if (m == bi) bound = -1.f;
   }
-  for (int p = 0; p < kSelPairs; ++p) sel[g * kSelPairs + p] = chosen[p];
 }
 
 // ---------------------------------------------------------------------------
@@ -144,6 +143,9 @@ __global__ void pair_select_kernel(const uint32_t* __restrict__ mxq,
 // pairs, and V^T.  A key is rotated once here instead of once per query block that
 // reads it.  One workgroup (256 threads) per (tile, KV head).
 // ---------------------------------------------------------------------------
+// INTERP: continuous remote positions (angles evaluated in fp64 here, no table); a
+// separate instantiation keeps the table path's register allocation small.
+template <bool INTERP>
 __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
   using namespace mf;
   __shared__ __align__(16) uint16_t sv[BK][D + 8];
@@ -170,9 +172,9 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
 
   const int tid = threadIdx.x;
   const int k = tid >> 3, p = tid & 7;  // key of the tile; pairs 8p .. 8p+7
-  const bool interp = args.interp != 0;
+  constexpr bool interp = INTERP;
   const double rpos = (double)(G - 1) / (double)G;  // continuous: n(x) = x - x/G = x rpos
-  if (interp) {
+  if constexpr (interp) {
     if (tid < D / 2) s_invf[tid] = inv_freq64(args.theta, tid, D);
     __syncthreads();
   }
@@ -671,7 +673,7 @@ hipError_t launch_pair_select(const void* Q, const void* K, int T, int Hq, int H
     hipLaunchKernelGGL(pair_max_kernel, dim3((Hkv * 64 + 255) / 256, ty), dim3(256), 0, stream,
                        (const uint16_t*)K, T, Hkv, tpb, mx + Hq * 64);
   }
-  hipLaunchKernelGGL(pair_select_kernel, dim3((Hkv + 63) / 64), dim3(64), 0, stream, mx,
+  hipLaunchKernelGGL(pair_select_kernel, dim3(Hkv), dim3(64), 0, stream, mx,
                      mx + Hq * 64, Hq, Hkv, sel);
   return hipGetLastError();
 }
@@ -693,7 +695,12 @@ static hipError_t launch_mfma_rep(const PrefillArgs& args, hipStream_t stream) {
 
 hipError_t launch_prefill_mfma(const PrefillArgs& args, int chunk_tiles, hipStream_t stream) {
   if (chunk_tiles > 0) {
-    hipLaunchKernelGGL(key_prep_kernel, dim3(chunk_tiles, args.Hkv), dim3(256), 0, stream, args);
+    if (args.interp)
+      hipLaunchKernelGGL(key_prep_kernel<true>, dim3(chunk_tiles, args.Hkv), dim3(256), 0, stream,
+                         args);
+    else
+      hipLaunchKernelGGL(key_prep_kernel<false>, dim3(chunk_tiles, args.Hkv), dim3(256), 0, stream,
+                         args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
