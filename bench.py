@@ -20,7 +20,14 @@ Prints one JSON line on stdout; progress goes to stderr.
   vanilla    the same calls with w0 >= L (every pair local, i.e. causal attention with
              standard RoPE, no remote branch): prefill and decode times and the bifocal /
              vanilla ratios, the local analogue of the pages' overhead figures
-  cpu_baseline  the CPU oracle timed on sampled query rows, extrapolated by pair count
+  cpu_baseline  the CPU oracle timed on sampled query rows, extrapolated by pair count;
+             also the host (CPU model, cores), the small prefill workload run whole and two
+             sampled steps of the 128K decode workload
+  executed_mfma  matrix-core FLOPs actually issued per launch (SQ_INSTS_VALU_MFMA_MOPS_*
+             counters, profiles/prefill_counters.json) over the measured time, with the
+             MFMA-busy and VALU/MFMA co-execution shares; null when the kernel source
+             changed after the counters were taken
+  ms_median  median prefill call time (ms_per_step is the mean over the timed calls)
   traffic    HBM bytes per launch of the timed kernel from rocprofv3 FETCH_SIZE and
              WRITE_SIZE counters (profiles/hbm_traffic.json), scaled by what the same
              counters read for a plain 1 GiB device copy (``--only copy``); null when
@@ -87,6 +94,21 @@ def hbm_traffic(kind):
         return None
 
 
+def mfma_counters(kind="prefill"):
+    """Executed MFMA FLOPs per launch and the MFMA busy / co-execution shares of the
+    timed kernel, from the committed counter summary; None if absent or taken on a
+    different kernel source."""
+    path = os.path.join(ROOT, "profiles", "prefill_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec["source_sha256"] != source_hash(kind):
+            return None
+        return rec["derived"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def bench_copy(torch, mib, reps):
     """A plain device copy of known size: the calibration run for the HBM byte counters."""
     n = mib * (1 << 20) // 4
@@ -131,17 +153,18 @@ def bench_prefill(bf, torch, W, steps, warmup, w0=None, three_pass=False):
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         call()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    per_call = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    ms = ev[0].elapsed_time(ev[steps]) / steps
     F, Fc = prefill_flops(w.seqlens, w.w0, w.Hq, w.D)
     assert bool(torch.isfinite(out).all())
-    return w, ms, F, Fc
+    return w, ms, F, Fc, float(np.median(per_call))
 
 
 def bench_decode(bf, torch, W, passes, warmup, w0=None):
@@ -246,11 +269,70 @@ def cpu_baseline(W, F, n_uniform=200):
     pairs_sampled = float(np.sum(rows + 1))
     pairs_total = L * (L + 1) / 2.0
     t_full = t * pairs_total / pairs_sampled
-    return {"value": F / t_full / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(rows)} query rows x {w.Hq} heads of qwen3_4b_128k "
-                      f"({t:.1f} s), extrapolated by causal pair count to all "
-                      f"{L} rows (t_full = {t_full:.0f} s)"}
+    out = {"value": F / t_full / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{len(rows)} query rows x {w.Hq} heads of qwen3_4b_128k "
+                     f"({t:.1f} s), extrapolated by causal pair count to all "
+                     f"{L} rows (t_full = {t_full:.0f} s)",
+           "host": host_info()}
+    out.update(cpu_other_configs(W))
+    return out
+
+
+def host_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cores": affinity}
+
+
+def cpu_other_configs(W):
+    """The oracle on the small prefill workload (whole, wall clock) and on the first and
+    last of the 256 steps of the 128K decode workload, extrapolated to all 256 (each
+    step rotates the whole 128K cache in float64: seconds per step)."""
+    from oracle.bifocal_ref import bifocal_decode_ref, bifocal_prefill_ref, rope_rotate
+    res = {}
+    w = W.get("tiny_f32")
+    q, k, v = W.raw_prefill_inputs(w)
+    pos = np.concatenate([np.arange(L) for L in w.seqlens])
+    Q = rope_rotate(q, pos, w.theta).astype(np.float32)
+    K = rope_rotate(k, pos, w.theta).astype(np.float32)
+    t0 = time.perf_counter()
+    bifocal_prefill_ref(Q, K, v.astype(np.float32), [int(c) for c in w.cu_seqlens], w.w0,
+                        w.w_pretrained, w.theta)
+    res["tiny_f32_full_s"] = round(time.perf_counter() - t0, 3)
+    w = W.get("qwen3_8b_decode_128k")
+    q, k, v = W.raw_decode_inputs(w)
+    S = k.shape[0]
+    Kc = np.empty(k.shape, dtype=np.float32)
+    for c0 in range(0, S, 16384):
+        Kc[c0:c0 + 16384] = W.round_to_bf16(
+            rope_rotate(k[c0:c0 + 16384], np.arange(c0, min(S, c0 + 16384)), w.theta))
+    Vc = W.round_to_bf16(v)
+    del k, v
+    positions = w.decode_positions()
+    idx = [0, len(positions) - 1]
+    t0 = time.perf_counter()
+    for i in idx:
+        p = int(positions[i])
+        qs = W.round_to_bf16(rope_rotate(q[i][None], [p], w.theta)[0])
+        bifocal_decode_ref(qs, Kc, Vc, p, w.w0, w.w_pretrained, w.theta)
+    t = time.perf_counter() - t0
+    res["decode_128k"] = {"s_per_step": round(t / len(idx), 3),
+                          "s_per_256_steps": round(t / len(idx) * len(positions), 1),
+                          "sample": f"steps at positions {int(positions[idx[0]])} and "
+                                    f"{int(positions[idx[-1]])}, x {len(positions) // len(idx)}"}
+    return res
 
 
 def main():
@@ -289,7 +371,7 @@ def main():
         return
     if args.only in ("all", "prefill"):
         log("prefill: qwen3_4b_128k")
-        w, ms, F, Fc = bench_prefill(bf, torch, W, args.steps, args.warmup)
+        w, ms, F, Fc, ms_med = bench_prefill(bf, torch, W, args.steps, args.warmup)
         tflops = F / (ms * 1e-3) / 1e12
         log(f"prefill: {ms:.2f} ms/call, {tflops:.1f} TFLOP/s counted, "
             f"{Fc / (ms * 1e-3) / 1e12:.1f} TFLOP/s causal-only")
@@ -304,11 +386,24 @@ def main():
                        "w_pretrained": w.w_pretrained, "G": 4, "theta": w.theta},
             "flops_per_step": F, "causal_flops_per_step": Fc,
             "causal_tflops": round(Fc / (ms * 1e-3) / 1e12, 3),
+            "ms_median": round(ms_med, 4),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": hbm_traffic("prefill")},
         })
+        mc = mfma_counters("prefill")
+        if mc is not None:
+            # matrix-core work actually issued (straddling tiles score twice, masked and
+            # padded lanes, the hi/lo correction step), from SQ_INSTS_VALU_MFMA_MOPS_*
+            result["executed_mfma"] = {
+                "flops_per_launch": mc["executed_flops"],
+                "tflops": round(mc["executed_flops"] / (ms * 1e-3) / 1e12, 3),
+                "ratio_to_counted": round(mc["executed_flops"] / F, 4),
+                "mfma_busy_frac": mc["mfma_busy_frac"],
+                "valu_mfma_coexec_frac": mc["coexec_frac"]}
+        else:
+            result["executed_mfma"] = None
     if args.only in ("all", "decode"):
         log("decode: qwen3_8b_decode_128k, 256 steps per pass")
         w, ms_step, kv_bytes = bench_decode(bf, torch, W, args.decode_passes,
@@ -339,7 +434,7 @@ def main():
                            "roofline": dec["roofline"], "decode_batch": dec.get("batch")})
     if not args.no_three_pass and args.only in ("all", "prefill"):
         log("three-pass prefill: qwen3_4b_128k, passes A, B, C + merge")
-        _, tms, _, _ = bench_prefill(bf, torch, W, args.steps, args.warmup, three_pass=True)
+        _, tms, _, _, _ = bench_prefill(bf, torch, W, args.steps, args.warmup, three_pass=True)
         result["three_pass"] = {"prefill_ms": round(tms, 4),
                                 "time_ratio_vs_fused": round(tms / result["ms_per_step"], 4)}
         log(f"three-pass prefill: {tms:.2f} ms, {tms / result['ms_per_step']:.3f}x the fused call")
@@ -348,8 +443,8 @@ def main():
                        "remote branch empty"}
         if args.only in ("all", "prefill"):
             log("vanilla prefill: qwen3_4b_128k with w0 = L")
-            wv, vms, _, Fc = bench_prefill(bf, torch, W, args.steps, args.warmup,
-                                           w0=W.get("qwen3_4b_128k").total_tokens)
+            wv, vms, _, Fc, _ = bench_prefill(bf, torch, W, args.steps, args.warmup,
+                                              w0=W.get("qwen3_4b_128k").total_tokens)
             van.update({"prefill_ms": round(vms, 4),
                         "prefill_causal_tflops": round(Fc / (vms * 1e-3) / 1e12, 3),
                         "prefill_time_ratio": round(result["ms_per_step"] / vms, 4)})
