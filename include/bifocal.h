@@ -31,6 +31,10 @@
  *     written.  BF_EHIP reports a failed launch (hipGetLastError after the launch);
  *     faults inside kernels surface at the caller's next stream synchronisation.
  *   - Supported head dims: D in {64, 128}.  Hq must be a multiple of Hkv.
+ *   - Lengths: a prefill sequence's length L and a decode step's pos + 1 must be below
+ *     2^24 (the range in which the aliased position floor(x / G) is formed with a
+ *     multiply and shift, exactly), and a prefill sequence's L * max(Hq, Hkv) * D below
+ *     2^31 (32-bit row offsets); BF_EUNSUPPORTED otherwise.
  *   - Thread safety: concurrent calls are safe on distinct workspaces.
  */
 #ifndef BIFOCAL_H_
