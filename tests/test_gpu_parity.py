@@ -444,6 +444,76 @@ def test_decode_variant_matches_oracle(bf, variant):
 
 
 # ---------------------------------------------------------------------------
+# an explicit softmax scale (flatter and sharper than 1/sqrt(D))
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scale", [0.03, 0.2])
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64)])
+def test_explicit_softmax_scale(bf, dt, D, scale):
+    w = W.Workload("scale", "prefill", dt, Hq=8, Hkv=2, D=D, w0=40, w_pretrained=128,
+                   theta=1e4, seqlens=(600, 77), outliers=0, seed=311)
+    say("prefill, softmax_scale", scale, w)
+    Q, K, V, cu = prefill_inputs(w)
+    O, lse = bf.bifocal_prefill(dev(Q, dt), dev(K, dt), dev(V, dt), [int(c) for c in cu],
+                                w.w0, w.w_pretrained, w.theta, softmax_scale=scale)
+    torch.cuda.synchronize()
+    Og, Lg = host(O), lse.cpu().numpy()
+    tol = BF16_TOL if dt == "bf16" else F32_TOL
+    ref = bifocal_prefill_ref(Q, K, V, cu, w.w0, w.w_pretrained, w.theta, scale=scale)
+    for b, (rows, Or, Lr) in enumerate(ref):
+        s0 = int(cu[b])
+        e = errors(Og[s0 + rows], Or, Lg[:, s0 + rows].T, Lr)
+        say(f"  seq {b} {e}")
+        assert within(e, tol), (b, e)
+    # decode over a cache with the same scale (matrix-core path for bf16 D = 128,
+    # vector path otherwise)
+    wd = W.Workload("scaled", "decode", dt, Hq=8, Hkv=2, D=D, w0=40, w_pretrained=128,
+                    theta=1e4, cache_len=900, decode_steps=2, outliers=0, seed=312)
+    q_raw, Kc, Vc = decode_inputs(wd)
+    for step, pos in enumerate((899, 130)):
+        q = std_query(q_raw[step], pos, wd.theta, dt)
+        o, l = bf.bifocal_decode(dev(q, dt), dev(Kc, dt), dev(Vc, dt), pos, wd.w0,
+                                 wd.w_pretrained, wd.theta, softmax_scale=scale)
+        torch.cuda.synchronize()
+        Or, Lr = bifocal_decode_ref(q, Kc, Vc, pos, wd.w0, wd.w_pretrained, wd.theta,
+                                    scale=scale)
+        e = errors(host(o), Or, l.cpu().numpy(), Lr)
+        say(f"  decode pos={pos} {e}")
+        assert within(e, tol), (pos, e)
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64)])
+def test_outputs_without_lse_are_identical(bf, dt, D):
+    # lse = NULL only skips the LSE stores: O is bit for bit the same
+    w = W.Workload("nolse", "prefill", dt, Hq=8, Hkv=2, D=D, w0=30, w_pretrained=100,
+                   theta=1e4, seqlens=(400, 33), outliers=4, seed=313)
+    say("outputs without lse", dt, D)
+    Q, K, V, cu = prefill_inputs(w)
+    Qd, Kd, Vd = dev(Q, dt), dev(K, dt), dev(V, dt)
+    c = [int(x) for x in cu]
+    calls = [("prefill", lambda want: bf.bifocal_prefill(Qd, Kd, Vd, c, w.w0, w.w_pretrained,
+                                                         w.theta, want_lse=want))]
+    if dt == "bf16":
+        calls.append(("prefill_ie", lambda want: bf.bifocal_prefill_ie(
+            Qd, Kd, Vd, c, w.w0, w.w_pretrained, w.theta, want_lse=want)))
+    qb = Qd[:3].contiguous()
+    Kb = torch.stack([Kd[:300], Kd[:300], Kd[:300]]).contiguous()
+    Vb = torch.stack([Vd[:300], Vd[:300], Vd[:300]]).contiguous()
+    calls.append(("decode", lambda want: bf.bifocal_decode(Qd[299], Kd, Vd, 299, w.w0,
+                                                           w.w_pretrained, w.theta,
+                                                           want_lse=want)))
+    calls.append(("decode_batch", lambda want: bf.bifocal_decode_batch(
+        qb, Kb, Vb, [299, 150, 0], w.w0, w.w_pretrained, w.theta, want_lse=want)))
+    for name, fn in calls:
+        o1, l1 = fn(True)
+        o2, l2 = fn(False)
+        torch.cuda.synchronize()
+        assert l1 is not None and l2 is None
+        assert torch.equal(o1, o2), name
+        assert bool(torch.isfinite(l1).all()), name
+
+
+# ---------------------------------------------------------------------------
 # launch chunking: more sequences than one launch takes
 # ---------------------------------------------------------------------------
 
