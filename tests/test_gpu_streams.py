@@ -1,0 +1,118 @@
+"""The calls on a non-default stream and under HIP-graph capture: the library only
+enqueues kernels on the caller's stream (no allocation, copy, memset or
+synchronisation), so a captured call replays to the eager result bit for bit.  Each
+graph is replayed several times with other eager work and synchronisations in between,
+and every replay is checked."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import decode_inputs, prefill_inputs, std_query
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def bf():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import dynamic_rope_context_amd as m
+    m.lib()  # raises if the library is missing
+    return m
+
+
+def dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(TDT[dt]).cuda()
+
+
+def _prefill_setup(bf, dt, D):
+    w = W.Workload("graphp", "prefill", dt, Hq=8, Hkv=2, D=D, w0=40, w_pretrained=128,
+                   theta=1e4, seqlens=(700, 90), outliers=4, seed=401)
+    Q, K, V, cu = prefill_inputs(w)
+    Qd, Kd, Vd = dev(Q, dt), dev(K, dt), dev(V, dt)
+    c = [int(x) for x in cu]
+    T = c[-1]
+    out = torch.empty_like(Qd)
+    lse = torch.empty((w.Hq, T), dtype=torch.float32, device="cuda")
+    ws = bf.Workspace.for_op(bf.OP_PREFILL, max(w.seqlens), w.Hq, w.Hkv, D, total_tokens=T,
+                             num_seqs=len(w.seqlens))
+    call = lambda: bf.bifocal_prefill(Qd, Kd, Vd, c, w.w0, w.w_pretrained, w.theta, out=out,
+                                      lse=lse, workspace=ws)
+    return call, out, lse
+
+
+def _decode_setup(bf, dt, D):
+    w = W.Workload("graphd", "decode", dt, Hq=8, Hkv=2, D=D, w0=40, w_pretrained=128,
+                   theta=1e4, cache_len=1500, decode_steps=1, outliers=4, seed=402)
+    q_raw, Kc, Vc = decode_inputs(w)
+    pos = 1499
+    qd = dev(std_query(q_raw[0], pos, w.theta, dt), dt)
+    Kd, Vd = dev(Kc, dt), dev(Vc, dt)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.Hq,), dtype=torch.float32, device="cuda")
+    ws = bf.Workspace.for_op(bf.OP_DECODE, 1500, w.Hq, w.Hkv, D)
+    call = lambda: bf.bifocal_decode(qd, Kd, Vd, pos, w.w0, w.w_pretrained, w.theta, out=out,
+                                     lse=lse, workspace=ws)
+    return call, out, lse
+
+
+SETUPS = {"prefill": _prefill_setup, "decode": _decode_setup}
+CASES = [("prefill", "bf16", 128), ("prefill", "f32", 64), ("decode", "bf16", 128),
+         ("decode", "f32", 64)]
+
+
+@pytest.mark.parametrize("what,dt,D", CASES)
+def test_non_default_stream(bf, what, dt, D):
+    say("stream", what, dt, D)
+    call, out, lse = SETUPS[what](bf, dt, D)
+    call()
+    torch.cuda.synchronize()
+    o_ref, l_ref = out.clone(), lse.clone()
+    out.zero_()
+    lse.zero_()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    s.synchronize()
+    assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
+
+
+@pytest.mark.parametrize("what,dt,D", CASES)
+def test_graph_replays_match_eager(bf, what, dt, D):
+    say("graph", what, dt, D)
+    call, out, lse = SETUPS[what](bf, dt, D)
+    call()  # eager: also sets the kernels' launch attributes before any capture
+    torch.cuda.synchronize()
+    o_ref, l_ref = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for r in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        scratch.mul_(1.0001)  # other eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref), (what, r)
+        assert torch.equal(lse, l_ref), (what, r)
+        call()  # an eager call between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref), (what, "eager", r)
