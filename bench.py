@@ -296,10 +296,44 @@ def host_info():
     return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cores": affinity}
 
 
+def _oracle_sampled(W, name, n_uniform):
+    """The oracle on sampled rows of each sequence of a prefill workload, for the first
+    quarter of the query heads, extrapolated per sequence by its causal pair count and
+    by the head count."""
+    from oracle.bifocal_ref import bifocal_rows, rope_rotate
+    w = W.get(name)
+    q, k, v = W.raw_prefill_inputs(w)
+    t_sample = t_full = 0.0
+    nrows = 0
+    heads = list(range(max(1, w.Hq // 4)))
+    for b, L in enumerate(w.seqlens):
+        s0 = int(w.cu_seqlens[b])
+        rows = W.sample_rows(L, w.w0, n_uniform, seed=w.seed + b, tile=64)
+        pos = np.arange(L)
+        Qs = W.round_to_bf16(rope_rotate(q[s0 + rows][:, :len(heads)], rows, w.theta)
+                             .astype(np.float32))
+        nkv = (heads[-1] // (w.Hq // w.Hkv)) + 1  # KV heads the timed query heads read
+        Ks = np.empty((L, nkv, w.D), dtype=np.float32)
+        for c0 in range(0, L, 16384):
+            c1 = min(L, c0 + 16384)
+            Ks[c0:c1] = rope_rotate(k[s0 + c0:s0 + c1, :nkv], pos[c0:c1], w.theta)
+        Ks, V = W.round_to_bf16(Ks), W.round_to_bf16(v[s0:s0 + L, :nkv])
+        t0 = time.perf_counter()
+        bifocal_rows(Qs, Ks, V, rows, w.w0, w.w_pretrained, w.theta, q_given_rows=True,
+                     heads=heads)
+        t = time.perf_counter() - t0
+        t_sample += t
+        nrows += len(rows)
+        t_full += t * (L * (L + 1) / 2.0) / float(np.sum(rows + 1)) * (w.Hq / len(heads))
+    return {"sampled_rows": nrows, "heads": f"{len(heads)} of {w.Hq}",
+            "t_sample_s": round(t_sample, 2), "t_full_s_extrapolated": round(t_full, 1)}
+
+
 def cpu_other_configs(W):
-    """The oracle on the small prefill workload (whole, wall clock) and on the first and
-    last of the 256 steps of the 128K decode workload, extrapolated to all 256 (each
-    step rotates the whole 128K cache in float64: seconds per step)."""
+    """The oracle on the small prefill workload (whole, wall clock), on sampled rows of
+    the 32K (G = 1) and ragged prefill workloads (extrapolated by pair count), and on
+    the first and last of the 256 steps of the 128K decode workload, extrapolated to
+    all 256 (each step rotates the whole 128K cache in float64: seconds per step)."""
     from oracle.bifocal_ref import bifocal_decode_ref, bifocal_prefill_ref, rope_rotate
     res = {}
     w = W.get("tiny_f32")
@@ -311,6 +345,8 @@ def cpu_other_configs(W):
     bifocal_prefill_ref(Q, K, v.astype(np.float32), [int(c) for c in w.cu_seqlens], w.w0,
                         w.w_pretrained, w.theta)
     res["tiny_f32_full_s"] = round(time.perf_counter() - t0, 3)
+    for name in ("qwen3_1p7b_32k_g1", "qwen3_8b_ragged"):
+        res[name] = _oracle_sampled(W, name, n_uniform=32)
     w = W.get("qwen3_8b_decode_128k")
     q, k, v = W.raw_decode_inputs(w)
     S = k.shape[0]
