@@ -36,6 +36,8 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import os
@@ -53,6 +55,19 @@ PEAK_HBM_GBS = 8000.0
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def quiet_host():
+    """A timed region without Python's cyclic garbage collector: a full collection after
+    the large setups can pause the submitting thread for tens of milliseconds, which a
+    launch-rate-bound loop (decode) would otherwise count as GPU time."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 
 KERNEL_SOURCES = {
@@ -155,11 +170,12 @@ def bench_prefill(bf, torch, W, steps, warmup, w0=None, three_pass=False):
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    ev[0].record(stream)
-    for i in range(steps):
-        call()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
+    with quiet_host():
+        ev[0].record(stream)
+        for i in range(steps):
+            call()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
     per_call = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     ms = ev[0].elapsed_time(ev[steps]) / steps
     F, Fc = prefill_flops(w.seqlens, w.w0, w.Hq, w.D)
@@ -191,11 +207,12 @@ def bench_decode(bf, torch, W, passes, warmup, w0=None):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(passes):
-        one_pass()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    with quiet_host():
+        e0.record(stream)
+        for _ in range(passes):
+            one_pass()
+        e1.record(stream)
+        torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / (passes * len(positions))
     kv_bytes = float(np.mean([2 * (p + 1) * w.Hkv * w.D * 2 for p in positions]))
     return w, ms_step, kv_bytes
@@ -228,11 +245,12 @@ def bench_decode_batch(bf, torch, W, passes, warmup, B=8, S=16384):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(passes):
-        one_pass()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    with quiet_host():
+        e0.record(stream)
+        for _ in range(passes):
+            one_pass()
+        e1.record(stream)
+        torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / (passes * steps) * 1e3
     kv = 2.0 * B * S * w.Hkv * w.D * 2
     return {"batch": B, "cache_rows_each": S, "us_per_step": round(us, 2),
