@@ -279,6 +279,19 @@ __device__ __forceinline__ void wait_vm_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// The same with a count per wave: wave 0 issues more transfers per tile (the ninth
+// key-operand KiB and the hi/lo correction rows) than the other waves.
+template <int N0, int N>
+__device__ __forceinline__ void wait_vm_barrier_w(int wave) {
+  static_assert(N0 >= 0 && N0 < 64 && N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  if (wave == 0)
+    __builtin_amdgcn_s_waitcnt((N0 & 15) | (7 << 4) | ((N0 >> 4) << 14));
+  else
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // One 16-byte LDS-DMA transfer per lane: lane l's 16 bytes land at dst + 16 l.
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
@@ -554,12 +567,13 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // landed (read in iterations v+1 and v+2); the younger transfers (tiles v+4 ..
   // v+PREF, at least two per tile) may still be in flight.  Iteration v refills the
   // slot of tile v-2, whose last reader (iteration v-2) is behind a barrier.
-  constexpr int kVmAhead = 2 * (PREF - 3);
+  constexpr int kVmAhead = 2 * (PREF - 3);    // waves 1..7: two transfers per tile
+  constexpr int kVmAhead0 = 3 * (PREF - 3);   // wave 0: three (local tile) or four
   if (nr > 0) load_q_remote();
   else load_q_std();
 #pragma unroll
   for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes);
-  wait_vm_barrier<kVmAhead>();  // tiles 0 .. 2 in LDS
+  wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);  // tiles 0 .. 2 in LDS
   f32x16 s_cur = nr > 0 ? qk_remote(0) : qk_local(0);
 
   // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
@@ -577,7 +591,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     uint32_t pk[8];
     softmax_exp(sc, pk);
     pv(pk, slot(v));
-    if (v & 1) wait_vm_barrier<kVmAhead>();
+    if (v & 1) wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);
   };
   f32x16 s_alt;
   auto run = [&](int& v, int end, auto qkrem_c, auto mk_c) __attribute__((always_inline)) {
