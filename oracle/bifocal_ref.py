@@ -58,6 +58,10 @@ equals vanilla causal RoPE attention (torch SDPA, float64); w0 = 1 equals pure
 aliased attention (torch SDPA on aliased rotations); every remote angle stays
 on the pretrained grid; rotations compose additively; RoPE against a
 complex-number formulation; decode equals the last prefill row.
+
+Parity unpinned where the pages fix nothing: they print no worked numeric example,
+so the readings above (rotate-half pairing, the sliding window, query offset 0) are
+checked for being computed as stated, not for being the pages' intent.
 """
 from __future__ import annotations
 
