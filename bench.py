@@ -70,16 +70,19 @@ def quiet_host():
         gc.enable()
 
 
+# Files that decide the timed kernels' machine code (sources and the build flags).
 KERNEL_SOURCES = {
     "prefill": ["dynamic_rope_context_amd/csrc/prefill_mfma.hip",
                 "dynamic_rope_context_amd/csrc/prefill_args.h",
                 "dynamic_rope_context_amd/csrc/mfma_util.h",
-                "dynamic_rope_context_amd/csrc/bf_common.h"],
+                "dynamic_rope_context_amd/csrc/bf_common.h",
+                "dynamic_rope_context_amd/build.py"],
     "decode": ["dynamic_rope_context_amd/csrc/decode_mfma.hip",
                "dynamic_rope_context_amd/csrc/decode.hip",
                "dynamic_rope_context_amd/csrc/decode_args.h",
                "dynamic_rope_context_amd/csrc/mfma_util.h",
-               "dynamic_rope_context_amd/csrc/bf_common.h"],
+               "dynamic_rope_context_amd/csrc/bf_common.h",
+               "dynamic_rope_context_amd/build.py"],
 }
 
 

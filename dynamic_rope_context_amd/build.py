@@ -21,6 +21,11 @@ ARCH = os.environ.get("BIFOCAL_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
+# Per-source additions.  The prefill kernel's softmax maxima are fmaxf chains over
+# MFMA results; without NaN semantics the compiler drops the canonicalizing moves it
+# puts before each of them (about 5 VALU instructions per 32-key tile and wave).  A NaN
+# in the inputs still reaches the output through the exponentials and PV.
+EXTRA_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:
@@ -38,7 +43,7 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
     def compile_one(src):
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"]
-        cmd = [hipcc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stderr}")
