@@ -298,6 +298,13 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0,
                                    0);
 }
+// The same from a wave-uniform base plus a 32-bit lane offset.  The empty asm keeps the
+// offset's zero extension next to the add, so the transfer takes the scalar-base form
+// instead of a 64-bit vector address computed per transfer.
+__device__ __forceinline__ void dma16_at(const uint8_t* base, uint32_t off, void* lds_dst) {
+  asm volatile("" : "+v"(off));
+  dma16(base + off, lds_dst);
+}
 
 template <int REP>
 __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
@@ -458,18 +465,18 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (q == 0 || wave == 0)
-          dma16(rec + krec_off[q], st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
-      if (wave == 0) dma16(rec + kRecKr + lane16, st + offsetof(Stage, kc));
+          dma16_at(rec, krec_off[q], st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
+      if (wave == 0) dma16_at(rec, kRecKr + lane16, st + offsetof(Stage, kc));
     } else {
       const uint8_t* kb = reinterpret_cast<const uint8_t*>(kseq);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (q == 0 || wave == 0) {
           const uint32_t j = min((uint32_t)(kt * BK) + krow_r[q], (uint32_t)(L - 1));
-          dma16(kb + (j * krow_bytes + kcol_b[q]), st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
+          dma16_at(kb, j * krow_bytes + kcol_b[q], st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
         }
     }
-    dma16(rec + (kRecKr + kRecKc + 1024 * wave) + lane16, st + offsetof(Stage, vt) + 1024 * wave);
+    dma16_at(rec, (kRecKr + kRecKc + 1024 * wave) + lane16, st + offsetof(Stage, vt) + 1024 * wave);
   };
   constexpr int kStageBytes = (int)sizeof(Stage);
   auto slot = [&](int v) __attribute__((always_inline)) { return (v % NSTAGE) * kStageBytes; };
