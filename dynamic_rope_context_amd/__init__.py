@@ -128,6 +128,43 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _stream_obj(stream, device):
+    """The torch stream object of a launch: the current stream, a torch stream, or a raw
+    HIP stream handle wrapped as an external stream."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+class _CallWorkspace:
+    """A workspace for one call that owns none: allocated (and its header cleared) on the
+    launch stream, and marked as used by that stream afterwards, so that the caching
+    allocator hands the memory to nobody else before the call's kernels are done."""
+
+    def __init__(self, workspace, stream, device, make):
+        self.given = workspace
+        self.stream = stream
+        self.device = device
+        self.make = make
+        self.ws = None
+
+    def __enter__(self):
+        if self.given is not None:
+            return self.given
+        s = _stream_obj(self.stream, self.device)
+        with torch.cuda.stream(s):
+            self.ws = self.make()
+        self._s = s
+        return self.ws
+
+    def __exit__(self, *exc):
+        if self.ws is not None:
+            self.ws.buf.record_stream(self._s)
+        return False
+
+
 def group_size(L: int, w_pretrained: int) -> int:
     """G = max(1, ceil(L / w_pretrained)) as the kernels compute it."""
     return int(lib().bifocal_group_size(int(L), int(w_pretrained)))
@@ -142,15 +179,18 @@ def workspace_bytes(op: int, max_len: int, Hq: int, Hkv: int, D: int,
 
 
 class Workspace:
-    """Caller-owned device workspace (zero-filled so that it starts with no table)."""
+    """Caller-owned device workspace, 256-byte aligned.  Only its first 256 bytes (the
+    position table's header) are cleared, on the current stream: every other byte is
+    written by the library before it is read."""
 
     def __init__(self, nbytes: int, device="cuda"):
         if nbytes <= 0:
             raise BifocalError("workspace size must be positive")
-        self.buf = torch.zeros(int(nbytes) + 256, dtype=torch.uint8, device=device)
+        self.buf = torch.empty(int(nbytes) + 256, dtype=torch.uint8, device=device)
         off = (-self.buf.data_ptr()) % 256
         self.ptr = self.buf.data_ptr() + off
         self.nbytes = int(nbytes)
+        self.buf[off:off + 256].zero_()
 
     @classmethod
     def for_op(cls, op: int, max_len: int, Hq: int, Hkv: int, D: int, device="cuda",
@@ -190,16 +230,16 @@ def _prefill(fn, op, Q, K, V, cu_seqlens, w0, w_pretrained, theta, softmax_scale
     cu_arr = (ctypes.c_int32 * len(cu))(*cu)
     _same(Q, K, V)
     out, lse = _outputs(Q, out, lse, want_lse, (Hq, T))
-    if workspace is None:
-        max_len = max([cu[b + 1] - cu[b] for b in range(B)] + [0])
-        workspace = Workspace.for_op(op, max(max_len, 1), Hq, Hkv, D, Q.device,
-                                     total_tokens=max(T, max_len, 1), num_seqs=max(B, 1))
-    _check(fn(
-        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
-        _dev(lse, "lse") if lse is not None else 0,
-        ctypes.cast(cu_arr, ctypes.c_void_p), B, Hq, Hkv, D, int(w0), int(w_pretrained),
-        float(theta), float(softmax_scale), _dtype_code(Q), workspace.ptr, workspace.nbytes,
-        _stream(stream)), what)
+    max_len = max([cu[b + 1] - cu[b] for b in range(B)] + [0])
+    make = lambda: Workspace.for_op(op, max(max_len, 1), Hq, Hkv, D, Q.device,
+                                    total_tokens=max(T, max_len, 1), num_seqs=max(B, 1))
+    with _CallWorkspace(workspace, stream, Q.device, make) as ws:
+        _check(fn(
+            _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
+            _dev(lse, "lse") if lse is not None else 0,
+            ctypes.cast(cu_arr, ctypes.c_void_p), B, Hq, Hkv, D, int(w0), int(w_pretrained),
+            float(theta), float(softmax_scale), _dtype_code(Q), ws.ptr, ws.nbytes,
+            _stream(stream)), what)
     return out, lse
 
 
@@ -244,13 +284,13 @@ def bifocal_decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, 
         raise BifocalError("the cache holds fewer than pos + 1 entries")
     _same(q, Kcache, Vcache)
     out, lse = _outputs(q, out, lse, want_lse, (Hq,))
-    if workspace is None:
-        workspace = Workspace.for_op(OP_DECODE, pos + 1, Hq, Hkv, D, q.device)
-    _check(lib().bifocal_decode(
-        _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
-        _dev(lse, "lse") if lse is not None else 0, int(pos), Hq, Hkv, D, int(w0),
-        int(w_pretrained), float(theta), float(softmax_scale), _dtype_code(q), workspace.ptr,
-        workspace.nbytes, _stream(stream)), "bifocal_decode")
+    make = lambda: Workspace.for_op(OP_DECODE, pos + 1, Hq, Hkv, D, q.device)
+    with _CallWorkspace(workspace, stream, q.device, make) as ws:
+        _check(lib().bifocal_decode(
+            _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
+            _dev(lse, "lse") if lse is not None else 0, int(pos), Hq, Hkv, D, int(w0),
+            int(w_pretrained), float(theta), float(softmax_scale), _dtype_code(q), ws.ptr,
+            ws.nbytes, _stream(stream)), "bifocal_decode")
     return out, lse
 
 
@@ -272,16 +312,15 @@ def bifocal_decode_batch(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Te
         raise BifocalError("q, caches and pos disagree on the batch")
     _same(q, Kcache, Vcache)
     out, lse = _outputs(q, out, lse, want_lse, (B, Hq))
-    if workspace is None:
-        workspace = Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
-                                     num_seqs=max(B, 1))
+    make = lambda: Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
+                                    num_seqs=max(B, 1))
     pos_arr = (ctypes.c_int32 * max(B, 1))(*pl)
-    _check(lib().bifocal_decode_batch(
-        _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
-        _dev(lse, "lse") if lse is not None else 0, ctypes.cast(pos_arr, ctypes.c_void_p), B, S,
-        Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale),
-        _dtype_code(q), workspace.ptr, workspace.nbytes, _stream(stream)),
-        "bifocal_decode_batch")
+    with _CallWorkspace(workspace, stream, q.device, make) as ws:
+        _check(lib().bifocal_decode_batch(
+            _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
+            _dev(lse, "lse") if lse is not None else 0, ctypes.cast(pos_arr, ctypes.c_void_p),
+            B, S, Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale),
+            _dtype_code(q), ws.ptr, ws.nbytes, _stream(stream)), "bifocal_decode_batch")
     return out, lse
 
 
@@ -325,14 +364,13 @@ def bifocal_decode_variant(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.
         raise BifocalError("q, caches and pos disagree on the batch")
     _same(q, Kcache, Vcache)
     out, lse = _outputs(q, out, lse, want_lse, (B, Hq))
-    if workspace is None:
-        workspace = Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
-                                     num_seqs=max(B, 1))
+    make = lambda: Workspace.for_op(OP_DECODE, max(pl + [0]) + 1, Hq, Hkv, D, q.device,
+                                    num_seqs=max(B, 1))
     pos_arr = (ctypes.c_int32 * max(B, 1))(*pl)
-    _check(lib().bifocal_decode_variant(
-        _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
-        _dev(lse, "lse") if lse is not None else 0, ctypes.cast(pos_arr, ctypes.c_void_p), B, S,
-        Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale), code,
-        _dtype_code(q), workspace.ptr, workspace.nbytes, _stream(stream)),
-        "bifocal_decode_variant")
+    with _CallWorkspace(workspace, stream, q.device, make) as ws:
+        _check(lib().bifocal_decode_variant(
+            _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
+            _dev(lse, "lse") if lse is not None else 0, ctypes.cast(pos_arr, ctypes.c_void_p),
+            B, S, Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale),
+            code, _dtype_code(q), ws.ptr, ws.nbytes, _stream(stream)), "bifocal_decode_variant")
     return out, lse

@@ -6,8 +6,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <mutex>
-#include <vector>
 
 #include "bf_common.h"
 #include "prefill_args.h"
@@ -19,13 +17,13 @@ extern "C" {
 
 namespace bifocal {
 hipError_t launch_table_ensure(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
-                               bool full, hipStream_t stream);
+                               hipStream_t stream);
 hipError_t launch_rope_apply(void* x, const int32_t* pos, int pos0, int T_, int H, int D,
                              double theta, int G, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& args, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs& args, int chunk_tiles, hipStream_t stream);
-hipError_t launch_pair_select(const void* Q, const void* K, int T, int Hq, int Hkv,
-                              uint32_t* mx, int32_t* sel, hipStream_t stream);
+hipError_t launch_pair_select(const void* Q, const void* K, const void* V, int T, int Hq,
+                              int Hkv, uint32_t* mx, int32_t* sel, hipStream_t stream);
 int prefill_f32_rows_per_block();
 int prefill_mfma_positions_per_block(int rep);
 
@@ -48,41 +46,12 @@ int32_t group_size(int64_t L, int32_t w_pre) {
   return (int32_t)std::max<int64_t>(1, G);
 }
 
-// Host-side memory of which workspaces already hold a table.  Only a hint for the
-// launch size of the table check: the device header decides validity.
-struct TableHint {
-  const void* ws;
-  double theta;
-  int D;
-  int n_valid;
-};
-std::mutex g_hint_mu;
-std::vector<TableHint> g_hints;
+// The table check/build: every block of the full grid reads the header and leaves at
+// once when the workspace already holds a table for (theta, D) with enough rows, so a
+// repeated call costs one short launch; the host keeps no record of workspaces.
 bf_status ensure_table(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
                        hipStream_t stream) {
-  bool believed = false;
-  {
-    std::lock_guard<std::mutex> lk(g_hint_mu);
-    for (auto& h : g_hints)
-      if (h.ws == ws && h.theta == theta && h.D == D && h.n_valid >= n_needed) believed = true;
-  }
-  hipError_t e = launch_table_ensure(ws, lay, D, theta, n_needed, !believed, stream);
-  if (e != hipSuccess) return BF_EHIP;
-  if (!believed) {
-    const long long want = ((long long)n_needed + 65535) / 65536 * 65536;
-    const int n_build = (int)std::min<long long>(want, lay.n_cap);
-    std::lock_guard<std::mutex> lk(g_hint_mu);
-    g_hints.erase(std::remove_if(g_hints.begin(), g_hints.end(),
-                                 [&](const TableHint& h) { return h.ws == ws; }),
-                  g_hints.end());
-    if (g_hints.size() >= 64) g_hints.erase(g_hints.begin());
-    g_hints.push_back(TableHint{ws, theta, D, n_build});
-  } else {
-    std::lock_guard<std::mutex> lk(g_hint_mu);
-    for (auto& h : g_hints)
-      if (h.ws == ws) h.n_valid = std::min(h.n_valid, lay.n_cap);
-  }
-  return BF_OK;
+  return launch_table_ensure(ws, lay, D, theta, n_needed, stream) == hipSuccess ? BF_OK : BF_EHIP;
 }
 
 // Shared by bifocal_prefill (ie = false) and bifocal_prefill_ie (ie = true: the three
@@ -137,10 +106,9 @@ bf_status prefill_impl(const void* Q, const void* K, const void* V, void* O, flo
 
   char* wsb = reinterpret_cast<char*>(ws);
   uint32_t* mx = reinterpret_cast<uint32_t*>(wsb + lay.scratch_off);
-  int32_t* sel = reinterpret_cast<int32_t*>(
-      wsb + lay.scratch_off + align_up((size_t)(Hq + Hkv) * 64 * sizeof(uint32_t), 256));
+  int32_t* sel = reinterpret_cast<int32_t*>(wsb + lay.scratch_off + pair_max_bytes(Hq, Hkv));
   if (dt == BF_BF16) {
-    if (launch_pair_select(Q, K, T, Hq, Hkv, mx, sel, st) != hipSuccess) return BF_EHIP;
+    if (launch_pair_select(Q, K, V, T, Hq, Hkv, mx, sel, st) != hipSuccess) return BF_EHIP;
   }
 
   PrefillArgs a{};
@@ -352,6 +320,8 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
     a.w0 = w0;
     a.scale_log2 = scale_log2;
     a.variant = variant;
+    a.hdr = reinterpret_cast<TableHeader*>(ws);
+    a.n_cap = lay.n_cap;
     for (int32_t b0 = 0; b0 < B; b0 += kDecodeMaxBatch) {
       const int nb = std::min<int32_t>(kDecodeMaxBatch, B - b0);
       int32_t mp = 0;

@@ -48,6 +48,12 @@ struct WsLayout {
 constexpr int kDecodeMaxSplits = 512;     // partials per query head (vector decode path)
 constexpr int kDecodeMaxParts = 128;      // partials per (sequence, query head), matrix-core path
 constexpr int kSelPairs = 4;  // RoPE pairs per KV head given the hi/lo correction
+// Per-KV-head record written by the prefill pre-pass: the kSelPairs corrected pairs, then
+// the power-of-two exponents e that keep the fp16 operands in range (remote queries of
+// the group, remote keys, values: each operand is multiplied by 2^-e before its fp16
+// rounding, and the product is scaled back exactly).
+constexpr int kSelStride = 8;
+constexpr int kSelExpQ = kSelPairs, kSelExpK = kSelPairs + 1, kSelExpV = kSelPairs + 2;
 constexpr size_t kKeyTileBytes = 17408;  // one prefill key-tile record (32 keys, D = 128)
 constexpr int kKeyTileKeys = 32;
 
@@ -62,6 +68,10 @@ inline size_t ie_bytes(int64_t T, int Hq, int D) {
   return 3 * (align_up((size_t)T * Hq * D * sizeof(float), 256) +
               align_up((size_t)Hq * T * sizeof(float), 256));
 }
+// Prefill pre-pass maxima: per (head, RoPE pair) of Q, K and V.
+inline size_t pair_max_bytes(int Hq, int Hkv) {
+  return align_up((size_t)(Hq + 2 * Hkv) * 64 * sizeof(uint32_t), 256);
+}
 inline size_t scratch_bytes(int op, int Hq, int Hkv, int D, int64_t nseq = 1) {
   if (op == 3) op = 1;  // the inclusion-exclusion prefill shares the prefill scratch
   if (op == 2) {
@@ -71,8 +81,7 @@ inline size_t scratch_bytes(int op, int Hq, int Hkv, int D, int64_t nseq = 1) {
     return align_up(vec > mfma ? vec : mfma, 256);
   }
   if (op == 1) {
-    const size_t mx = align_up((size_t)(Hq + Hkv) * 64 * sizeof(uint32_t), 256);
-    return mx + align_up((size_t)Hkv * kSelPairs * sizeof(int32_t), 256);
+    return pair_max_bytes(Hq, Hkv) + align_up((size_t)Hkv * kSelStride * sizeof(int32_t), 256);
   }
   return 0;
 }

@@ -49,6 +49,11 @@ struct DecodeBatchArgs {
                             // workgroups, nwg <= kDecodeMaxParts
   float scale_log2;         // softmax scale * log2(e)
   int32_t variant;          // kVariant*
+  // The workspace's position-table header and the rows the table region holds in this
+  // call's layout: the partials sit past them and may overwrite rows a larger earlier
+  // table held, so the kernel lowers the header's row count to n_cap.
+  TableHeader* hdr;
+  int32_t n_cap;
   DecSeq seq[kDecodeMaxBatch];
 };
 

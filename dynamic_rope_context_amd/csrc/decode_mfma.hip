@@ -114,6 +114,12 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, kq = lane >> 4;  // MFMA column / row, K group
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    // table rows past this layout's capacity are overwritten by the partials below:
+    // a later prefill on the same workspace must not trust them
+    volatile TableHeader* h = a.hdr;
+    if (h->n_valid > a.n_cap) h->n_valid = a.n_cap;
+  }
 
   // Workgroup -> (sequence, group of NWD splits, KV head)
   const int id = blockIdx.x;

@@ -12,7 +12,7 @@ constexpr int kMaxSeqPerLaunch = 48;
 // kRecKeys keys of one sequence):
 //   kr  [kRecKeys][128]  fp16  R(f(j) - j) K_j                 8192 B
 //   kc  [kRecKeys][16]   fp16  hi/lo of the selected pairs     1024 B
-//   vt  [128][kRecKeys]  bf16  V^T                             8192 B
+//   vt  [128][kRecKeys]  fp16  V^T * 2^-e_v                    8192 B
 // Keys past the end of the sequence are zero.
 constexpr int kRecKeys = 32;
 constexpr size_t kRecKr = 8192, kRecKc = 1024, kRecVt = 8192;
@@ -36,7 +36,7 @@ struct PrefillArgs {
   void* O;
   float* lse;          // [Hq, T] or null
   const float2* tab;   // position table (cos, sin) [n][D/2]
-  const int32_t* sel;  // [Hkv][kSelPairs] RoPE pairs given the hi/lo correction
+  const int32_t* sel;  // [Hkv][kSelStride]: corrected RoPE pairs, operand exponents
   uint8_t* rec;        // key-tile records [Hkv][tiles_total] (bf16 path)
   double theta;        // RoPE base (angles evaluated in the kernels: continuous positions)
   int32_t T, Hq, Hkv, D, w0, nseq, max_qblocks, tiles_total;

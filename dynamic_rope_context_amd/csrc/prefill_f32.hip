@@ -130,13 +130,10 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs args) {
 template <int D>
 static hipError_t launch_f32_d(const PrefillArgs& args, hipStream_t stream) {
   const size_t sm = (3 * kRows * (D + 1) + 3 * kKeys * D) * sizeof(float);
-  static bool attr_set = false;  // benign race: every caller sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_f32_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch (idempotent, a host-side call): the library keeps no state
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_f32_kernel<D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  if (e != hipSuccess) return e;
   dim3 grid(args.max_qblocks * args.nseq, args.Hq);
   hipLaunchKernelGGL(prefill_f32_kernel<D>, grid, dim3(64), sm, stream, args);
   return hipGetLastError();

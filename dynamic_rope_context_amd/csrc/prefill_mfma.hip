@@ -30,9 +30,14 @@
 //     rounded to fp16 (same MFMA rate as bf16 on gfx950, 3 more mantissa bits), and
 //     for the 4 RoPE pairs per KV head with the largest |q||k| bound a hi/lo split adds
 //     one K=16 MFMA step (hi*lo + lo*hi) so that outlier channels do not lose the
-//     low-order bits of their products.
+//     low-order bits of their products.  Operands near the fp16 range are first scaled
+//     by exact powers of two chosen from the pre-pass maxima (undone in the softmax
+//     scale and the output), so no input a bf16 tensor can hold overflows them.
 //   * Online softmax in the base-2 domain with a lazy running max (rescale only when
-//     the max grows by more than 8), row sums kept per lane half.
+//     the max grows by more than 8), row sums kept per lane half.  P and V^T enter the
+//     PV product as fp16: with the lazy max a probability reaches 2^8, and a bf16 P
+//     (8 significant bits) would put up to 2^-9 of relative error into the row sum, the
+//     largest single term of the LSE error; fp16 keeps 11 bits at the same MFMA rate.
 //   * The same kernel also runs the three passes of the pages' inclusion-exclusion
 //     form (mode 1: remote over all causal pairs, 2: remote over the window, 3: local
 //     over the window) and the continuous-position variant (remote angles x/G - x
@@ -68,7 +73,7 @@ constexpr float kLazy = 8.f;  // allowed growth of the running max before a resc
 struct Stage {
   uint16_t k[K_DMA * 512];  // key operand: remote fp16 or standard bf16, padded rows
   uint16_t kc[BK * KC_LD];  // [lo of 8 selected channels | hi of them], fp16 bits
-  uint16_t vt[D * VT_LD];   // V^T, bf16 bits, swizzled chunks (see VT_LD)
+  uint16_t vt[D * VT_LD];   // V^T 2^-e_v, fp16 bits, swizzled chunks (see VT_LD)
 };
 static_assert(sizeof(Stage) == 18432, "stage = 18 KiB");
 constexpr int NSTAGE = 8;          // LDS ring of virtual tiles
@@ -107,9 +112,21 @@ __global__ void __launch_bounds__(256) pair_max_kernel(const uint16_t* __restric
   atomicMax(mx + hm, __float_as_uint(best));  // non-negative floats order as integers
 }
 
-// Top kSelPairs pairs per KV head by the bound max|k_m| * max_h |q_{h,m}| (squared).
+// Smallest e >= 0 with sqrt(m) * 2^-e < 2^15, for a maximum squared pair norm m: every
+// component of a pair (rotated or not) scaled by 2^-e then fits fp16 (max 65504).
+__device__ __forceinline__ int fp16_range_exp(float m) {
+  if (!(m > 0x1p30f)) return 0;
+  if (!(m < INFINITY)) return 64;
+  int x;
+  frexpf(m, &x);  // m < 2^x
+  return (x - 29) >> 1;
+}
+
+// Per KV head: the top kSelPairs pairs by the bound max|k_m| * max_h |q_{h,m}| (squared),
+// and the operand exponents of the group's remote queries, remote keys and values.
 __global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restrict__ mxq,
                                                          const uint32_t* __restrict__ mxk,
+                                                         const uint32_t* __restrict__ mxv,
                                                          int Hq, int Hkv,
                                                          int32_t* __restrict__ sel) {
   // one wave per KV head, lane = RoPE pair; kSelPairs rounds of a wave-wide argmax
@@ -118,7 +135,10 @@ __global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restr
   const int rep = Hq / Hkv;
   float q = 0.f;
   for (int r = 0; r < rep; ++r) q = fmaxf(q, __uint_as_float(mxq[(g * rep + r) * 64 + m]));
-  float bound = q * __uint_as_float(mxk[g * 64 + m]);  // >= 0
+  const float kk = __uint_as_float(mxk[g * 64 + m]);
+  float vv = __uint_as_float(mxv[g * 64 + m]);
+  float bound = q * kk;  // >= 0
+  float qm = q, km = kk;
   for (int p = 0; p < kSelPairs; ++p) {
     float bv = bound;
     int bi = m;
@@ -131,16 +151,28 @@ __global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restr
         bi = oi;
       }
     }
-    if (m == 0) sel[g * kSelPairs + p] = bi;
+    if (m == 0) sel[g * kSelStride + p] = bi;
     if (m == bi) bound = -1.f;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    qm = fmaxf(qm, __shfl_xor(qm, o));
+    km = fmaxf(km, __shfl_xor(km, o));
+    vv = fmaxf(vv, __shfl_xor(vv, o));
+  }
+  if (m == 0) {
+    sel[g * kSelStride + kSelExpQ] = fp16_range_exp(qm);
+    sel[g * kSelStride + kSelExpK] = fp16_range_exp(km);
+    sel[g * kSelStride + kSelExpV] = fp16_range_exp(vv);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Key preparation: once per call, each key tile of each KV head is turned into the
 // record the main kernel copies into LDS verbatim (layout in prefill_args.h): the
-// remote copy R(f(j) - j) K_j rounded to fp16, the hi/lo correction of the selected
-// pairs, and V^T.  A key is rotated once here instead of once per query block that
+// remote copy R(f(j) - j) K_j 2^-e_k rounded to fp16, the hi/lo correction of the
+// selected pairs, and V^T 2^-e_v in fp16 (the PV operands are fp16: P keeps 11
+// significant bits instead of 8).  A key is rotated once here instead of once per query block that
 // reads it.  One workgroup (256 threads) per (tile, KV head).
 // ---------------------------------------------------------------------------
 // INTERP: continuous remote positions (angles evaluated in fp64 here, no table); a
@@ -182,11 +214,23 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
   const bool valid = j < L;
   const size_t row_off = ((size_t)(start + min(j, L - 1)) * Hkv + g) * D;
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  // exact power-of-two operand scales (1 unless an input is near the fp16 range)
+  const float ks = __builtin_ldexpf(1.f, -args.sel[g * kSelStride + kSelExpK]);
+  const float vs = __builtin_ldexpf(1.f, -args.sel[g * kSelStride + kSelExpV]);
   {
     const uint4 v0 = valid ? *reinterpret_cast<const uint4*>(Vp + row_off + 8 * p) : zero;
     const uint4 v1 = valid ? *reinterpret_cast<const uint4*>(Vp + row_off + 64 + 8 * p) : zero;
-    *reinterpret_cast<uint4*>(&sv[k][8 * p]) = v0;
-    *reinterpret_cast<uint4*>(&sv[k][64 + 8 * p]) = v1;
+    uint4 h0, h1;
+    h0.x = pack_f16(bf16_at(v0, 0) * vs, bf16_at(v0, 1) * vs);
+    h0.y = pack_f16(bf16_at(v0, 2) * vs, bf16_at(v0, 3) * vs);
+    h0.z = pack_f16(bf16_at(v0, 4) * vs, bf16_at(v0, 5) * vs);
+    h0.w = pack_f16(bf16_at(v0, 6) * vs, bf16_at(v0, 7) * vs);
+    h1.x = pack_f16(bf16_at(v1, 0) * vs, bf16_at(v1, 1) * vs);
+    h1.y = pack_f16(bf16_at(v1, 2) * vs, bf16_at(v1, 3) * vs);
+    h1.z = pack_f16(bf16_at(v1, 4) * vs, bf16_at(v1, 5) * vs);
+    h1.w = pack_f16(bf16_at(v1, 6) * vs, bf16_at(v1, 7) * vs);
+    *reinterpret_cast<uint4*>(&sv[k][8 * p]) = h0;
+    *reinterpret_cast<uint4*>(&sv[k][64 + 8 * p]) = h1;
   }
   // G = 1 in the bifocal mode: every pair is local, the remote copy is never read (the
   // inclusion-exclusion passes read it whatever G is)
@@ -212,6 +256,11 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
         rot_neg(bf16_at(a, 2 * e2 + 1), bf16_at(c, 2 * e2 + 1), cs.z, cs.w, y1[2 * e2 + 1],
                 y2[2 * e2 + 1]);
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y1[e] *= ks;
+        y2[e] *= ks;
+      }
       y1p = make_uint4(pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
                        pack_f16(y1[6], y1[7]));
       y2p = make_uint4(pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]), pack_f16(y2[4], y2[5]),
@@ -226,15 +275,15 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
       const int jc = kt * BK + ck;
       uint32_t h1 = 0, l1 = 0, h2 = 0, l2 = 0;
       if (jc < L) {
-        const int m = args.sel[g * kSelPairs + cp];
+        const int m = args.sel[g * kSelStride + cp];
         const uint16_t* row = Kp + ((size_t)(start + jc) * Hkv + g) * D;
         const float2 cs = interp ? angle_cs(jc * rpos, s_invf[m])
                                  : tab[(size_t)(jc - alias_fast(jc, gdiv)) * 64 + m];
         float z1, z2;
         rot_neg(__uint_as_float((uint32_t)row[m] << 16), __uint_as_float((uint32_t)row[m + 64] << 16),
                 cs.x, cs.y, z1, z2);
-        split_f16(z1, h1, l1);
-        split_f16(z2, h2, l2);
+        split_f16(z1 * ks, h1, l1);
+        split_f16(z2 * ks, h2, l2);
       }
       uint16_t* crow = kc + ck * 16;
       const int lo_at = 8 * ((ck >> 3) & 1), hi_at = 8 - lo_at;  // swizzled chunks
@@ -392,6 +441,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
   };
+  const float qs = __builtin_ldexpf(1.f, -args.sel[g * kSelStride + kSelExpQ]);
   auto load_q_remote = [&]() __attribute__((always_inline)) {
     const int n = qrow_i - alias_fast(qrow_i, gdiv);
     uint4 raw[8];
@@ -406,6 +456,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         const float2 cs = interp ? angle_cs(qrow_i * rpos, s_invf[16 * s + 8 * hf + e])
                                  : trow[16 * s + 8 * hf + e];
         rot_neg(bf16_at(raw[s], e), bf16_at(raw[s + 4], e), cs.x, cs.y, y1[e], y2[e]);
+        y1[e] *= qs;
+        y2[e] *= qs;
       }
       qop[s] = u32x4{pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
                      pack_f16(y1[6], y1[7])};
@@ -415,15 +467,15 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     uint32_t part[8];
 #pragma unroll
     for (int p = 0; p < kSelPairs; ++p) {
-      const int m = args.sel[g * kSelPairs + p];
+      const int m = args.sel[g * kSelStride + p];
       const float x1 = __uint_as_float((uint32_t)qrow[m] << 16);
       const float x2 = __uint_as_float((uint32_t)qrow[m + 64] << 16);
       const float2 cs = interp ? angle_cs(qrow_i * rpos, s_invf[m]) : trow[m];
       float y1, y2;
       rot_neg(x1, x2, cs.x, cs.y, y1, y2);
       uint32_t h1, l1, h2, l2;
-      split_f16(y1, h1, l1);
-      split_f16(y2, h2, l2);
+      split_f16(y1 * qs, h1, l1);
+      split_f16(y2 * qs, h2, l2);
       part[p] = hf ? l1 : h1;
       part[p + 4] = hf ? l2 : h2;
     }
@@ -484,7 +536,10 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // ---- softmax state and output accumulators --------------------------------------
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};  // O^T blocks [d block]
   float m_run = -1e30f, l_run = 0.f;
-  const float c2 = args.scale * 1.4426950408889634f;  // scale * log2(e)
+  const float c2l = args.scale * 1.4426950408889634f;  // scale * log2(e): local scores
+  // remote scores come from operands scaled by 2^-e_q and 2^-e_k
+  const float c2r = __builtin_ldexpf(c2l, args.sel[g * kSelStride + kSelExpQ] +
+                                              args.sel[g * kSelStride + kSelExpK]);
 
   // Scores S^T (32 keys x this wave's 32 queries) of one virtual tile.
   auto qk_remote = [&](int so) __attribute__((always_inline)) -> f32x16 {
@@ -510,7 +565,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // Online softmax, part 1: masks, tile row max and the lazy rescale.  MK = 1: remote
   // pass over a straddling tile, keep i - j >= w0.  MK = 2: local pass over a straddling
   // or diagonal tile, keep 0 <= i - j < w0 (window and causality in one unsigned compare).
-  auto softmax_prep = [&](int v, f32x16& sacc, auto mk_c) __attribute__((always_inline)) {
+  auto softmax_prep = [&](int v, f32x16& sacc, float c2, auto mk_c) __attribute__((always_inline)) {
     constexpr int MK = decltype(mk_c)::value;
     if constexpr (MK != 0) {
       const int kt = vt_kt(v);
@@ -536,21 +591,22 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       m_run = m_new;
     }
   };
-  // Part 2: probabilities in the PV operand layout (bf16) and the row-sum update.  The
-  // row sum adds the same bf16-rounded probabilities that PV multiplies (two per
-  // v_dot2 against (1, 1), fp32 accumulation), so numerator and denominator agree.
-  auto softmax_exp = [&](const f32x16& sacc, uint32_t* pk) __attribute__((always_inline)) {
+  // Part 2: probabilities in the PV operand layout (fp16, round to nearest even) and the
+  // row-sum update.  The row sum adds the same rounded probabilities that PV multiplies
+  // (two per v_dot2 against (1, 1), fp32 accumulation), so numerator and denominator
+  // agree.
+  auto softmax_exp = [&](const f32x16& sacc, uint32_t* pk, float c2) __attribute__((always_inline)) {
     const float mneg = -m_run;
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     float l0 = l_run, l1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = fast_exp2(__fmaf_rn(sacc[r], c2, mneg));
       const float p1 = fast_exp2(__fmaf_rn(sacc[r + 1], c2, mneg));
-      pk[r / 2] = pack_bf16(p0, p1);
+      const f16x2 ph = {(_Float16)p0, (_Float16)p1};
+      pk[r / 2] = __builtin_bit_cast(uint32_t, ph);
       float& acc = (r & 2) ? l1 : l0;
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r / 2]), ones, acc,
-                                            false);
+      acc = __builtin_amdgcn_fdot2(ph, ones, acc, false);
     }
     l_run = l0 + l1;
   };
@@ -563,7 +619,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       const uint16_t* vrow = st.vt + ln * VT_LD + 8 * ((2 * t + hf) ^ ((ln >> 2) & 3));
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        oacc[db] = mfma_bf16(*reinterpret_cast<const u32x4*>(vrow + 32 * VT_LD * db), pb, oacc[db]);
+        oacc[db] = mfma_f16(*reinterpret_cast<const u32x4*>(vrow + 32 * VT_LD * db), pb, oacc[db]);
     }
   };
 
@@ -593,10 +649,11 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     // Tile v's row max and rescale first, so that tile v+1's score MFMAs and tile v's
     // exponentials (independent of each other) share one basic block and interleave.
     f32x16 sc = s_in;
-    softmax_prep(v, sc, mk_c);
+    const float c2 = v < nr ? c2r : c2l;  // class of tile v (wave-uniform)
+    softmax_prep(v, sc, c2, mk_c);
     s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
     uint32_t pk[8];
-    softmax_exp(sc, pk);
+    softmax_exp(sc, pk, c2);
     pv(pk, slot(v));
     if (v & 1) wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);
   };
@@ -648,7 +705,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // ---- epilogue: O = O^T / l, LSE ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qi < L) {
-    const float inv = 1.f / l_tot;
+    // O = (V 2^-e_v)^T P^T 2^e_v / l
+    const float inv = __builtin_ldexpf(1.f, args.sel[g * kSelStride + kSelExpV]) / l_tot;
     const size_t orow_off = ((size_t)(start + qi) * Hq + qhead) * D;
     if (args.out_f32) {
       float* orow = (float*)args.O + orow_off;
@@ -682,9 +740,10 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_pair_select(const void* Q, const void* K, int T, int Hq, int Hkv,
-                              uint32_t* mx /*[(Hq+Hkv)*64]*/, int32_t* sel, hipStream_t stream) {
-  const int n = (Hq + Hkv) * 64;
+hipError_t launch_pair_select(const void* Q, const void* K, const void* V, int T, int Hq,
+                              int Hkv, uint32_t* mx /*[(Hq+2Hkv)*64]*/, int32_t* sel,
+                              hipStream_t stream) {
+  const int n = (Hq + 2 * Hkv) * 64;
   hipLaunchKernelGGL(pair_max_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, mx, n);
   const int tpb = 256;  // tokens per block
   const int ty = (T + tpb - 1) / tpb;
@@ -693,22 +752,20 @@ hipError_t launch_pair_select(const void* Q, const void* K, int T, int Hq, int H
                        (const uint16_t*)Q, T, Hq, tpb, mx);
     hipLaunchKernelGGL(pair_max_kernel, dim3((Hkv * 64 + 255) / 256, ty), dim3(256), 0, stream,
                        (const uint16_t*)K, T, Hkv, tpb, mx + Hq * 64);
+    hipLaunchKernelGGL(pair_max_kernel, dim3((Hkv * 64 + 255) / 256, ty), dim3(256), 0, stream,
+                       (const uint16_t*)V, T, Hkv, tpb, mx + (Hq + Hkv) * 64);
   }
   hipLaunchKernelGGL(pair_select_kernel, dim3(Hkv), dim3(64), 0, stream, mx,
-                     mx + Hq * 64, Hq, Hkv, sel);
+                     mx + Hq * 64, mx + (Hq + Hkv) * 64, Hq, Hkv, sel);
   return hipGetLastError();
 }
 
 template <int REP>
 static hipError_t launch_mfma_rep(const PrefillArgs& args, hipStream_t stream) {
-  static bool attr_set = false;  // benign race: every caller sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_mfma_kernel<REP>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)mf::kSmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch (idempotent, a host-side call): the library keeps no state
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_mfma_kernel<REP>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)mf::kSmem);
+  if (e != hipSuccess) return e;
   const int blocks = args.Hkv * args.nseq * args.max_qblocks;
   hipLaunchKernelGGL(prefill_mfma_kernel<REP>, dim3(blocks), dim3(512), mf::kSmem, stream, args);
   return hipGetLastError();

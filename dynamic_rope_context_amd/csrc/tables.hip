@@ -67,10 +67,10 @@ __global__ void table_publish_kernel(TableHeader* hdr, int n_cap, int n_build, i
   h->magic = kTableMagic;
 }
 
-// Enqueue the table check/build.  `full` selects a grid that builds quickly; a
-// one-block launch still builds (slowly) if the header turns out to be stale.
+// Enqueue the table check/build (the full grid: a valid header sends every block home
+// after one load).
 hipError_t launch_table_ensure(void* ws, const WsLayout& lay, int D, double theta, int n_needed,
-                               bool full, hipStream_t stream) {
+                               hipStream_t stream) {
   TableHeader* hdr = reinterpret_cast<TableHeader*>(ws);
   float2* tab = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + lay.table_off);
   // Build ahead of need (to the next multiple of 64K positions, within capacity) so
@@ -78,7 +78,7 @@ hipError_t launch_table_ensure(void* ws, const WsLayout& lay, int D, double thet
   const long long want = ((long long)n_needed + 65535) / 65536 * 65536;
   const int n_build = (int)(want < lay.n_cap ? want : lay.n_cap);
   size_t total = (size_t)n_build * (D / 2);
-  int blocks = full ? (int)((total + 255) / 256) : 1;
+  int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(table_build_kernel, dim3(blocks), dim3(256), 0, stream, hdr, tab, n_build,

@@ -1,0 +1,87 @@
+"""The bf16 prefill's precision scheme, weighed on the CPU with a model of its rounding
+steps (tests/precision_model.py) against the float64 oracle, on the workloads' own input
+distribution: i.i.d. normal q/k/v with 4 independently seeded x8 outlier channels per
+query head and per KV head (the Qwen3-4B 128K and ragged workloads' layout), at
+GQA ratios 2 and 4.
+
+The bound checked is the LSE tolerance of the bf16 parity tests (5e-3) with margin: the
+scheme the kernel uses must stay at or below 3.5e-3 on the smoke workload and the many-
+short-sequences case, and at or below 4e-3 (80% of the bound) on every seed of the
+outlier layouts.  What remains is the fp16 rounding of every remote operand: an outlier
+channel (x8) makes both its query and its key rounding errors large (each is relative to
+the product |q_c k_c|), and at GQA ratio 4 a KV group carries up to 20 outlier pairs,
+beyond what a fixed set of corrected pairs covers cheaply.  The model is first
+tied to the oracle (with every remote channel corrected and fp16 probabilities it must
+agree to a few 1e-4) and to the kernel's measured behaviour (the earlier scheme, bf16
+probabilities, must show the 4.9e-3 the kernel measured on the smoke workload)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import prefill_inputs
+from oracle.bifocal_ref import bifocal_rows
+from precision_model import Scheme, emulate_rows, select_pairs
+
+KERNEL = Scheme(pairs=4, p_type="f16")     # what the matrix-core prefill does
+EARLIER = Scheme(pairs=4, p_type="bf16")   # bf16 probabilities
+EXACT = Scheme(pairs=64, p_type="f16")     # every remote channel corrected
+LSE_MARGIN = 3.5e-3
+LSE_MARGIN_LAYOUT = 4e-3
+
+SMOKE = W.Workload("smoke", "prefill", "bf16", Hq=8, Hkv=2, D=128, w0=64, w_pretrained=256,
+                   theta=1e6, seqlens=(1000, 77), outliers=4, seed=2024)
+
+
+def _errors(w, scheme, n_uniform=None):
+    """Worst (max |dO|, mean |dO|, max |dLSE|) of the model against the oracle over the
+    sequences of w (all rows, or sampled rows)."""
+    Q, K, V, cu = prefill_inputs(w)
+    pairs = select_pairs(Q, K, scheme.pairs)  # the pre-pass sees the whole packed call
+    worst = [0.0, 0.0, 0.0]
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        L = s1 - s0
+        rows = np.arange(L) if n_uniform is None else W.sample_rows(L, w.w0, n_uniform, seed=b)
+        Or, Lr = bifocal_rows(Q[s0:s1], K[s0:s1], V[s0:s1], rows, w.w0, w.w_pretrained, w.theta)
+        O, LSE = emulate_rows(Q[s0:s1], K[s0:s1], V[s0:s1], rows, w.w0, w.w_pretrained,
+                              w.theta, scheme, pairs=pairs)
+        d = np.abs(O - Or)
+        worst = [max(worst[0], d.max()), max(worst[1], d.mean()),
+                 max(worst[2], np.abs(LSE - Lr).max())]
+    return worst
+
+
+def test_model_with_exact_scores_matches_oracle():
+    # only the output and probability roundings left: the model's masks, tile order and
+    # softmax must reproduce the oracle closely
+    mx, mean, lse = _errors(SMOKE, EXACT)
+    assert lse < 6e-4 and mx < 1e-2 and mean < 1e-3, (mx, mean, lse)
+
+
+def test_model_reproduces_the_earlier_kernel_margin():
+    # bf16 probabilities: the kernel measured max |dLSE| 4.94e-3 on this workload
+    _, _, lse = _errors(SMOKE, EARLIER)
+    assert 4.5e-3 < lse < 5.5e-3, lse
+
+
+def test_kernel_scheme_on_smoke_workload():
+    mx, mean, lse = _errors(SMOKE, KERNEL)
+    assert lse <= LSE_MARGIN and mx <= 2e-2 and mean <= 2e-3, (mx, mean, lse)
+
+
+def test_kernel_scheme_on_many_short_sequences():
+    lens = tuple([(37 * i) % 150 + 1 for i in range(24)])
+    w = W.Workload("stress", "prefill", "bf16", Hq=4, Hkv=2, D=128, w0=20, w_pretrained=100,
+                   theta=1e6, seqlens=lens, outliers=4, seed=17)
+    mx, mean, lse = _errors(w, KERNEL)
+    assert lse <= LSE_MARGIN and mx <= 2e-2 and mean <= 2e-3, (mx, mean, lse)
+
+
+@pytest.mark.parametrize("rep", [2, 4])
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
+def test_kernel_scheme_on_workload_outlier_layout(rep, seed):
+    # G = 4 (L = 2048, w_pretrained = 512), a window of 128 keys, four KV heads
+    w = W.Workload("layout", "prefill", "bf16", Hq=4 * rep, Hkv=4, D=128, w0=128,
+                   w_pretrained=512, theta=1e6, seqlens=(2048,), outliers=4, seed=seed)
+    mx, mean, lse = _errors(w, KERNEL, n_uniform=200)
+    assert lse <= LSE_MARGIN_LAYOUT and mx <= 2e-2 and mean <= 2e-3, (mx, mean, lse)
