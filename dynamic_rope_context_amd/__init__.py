@@ -18,13 +18,14 @@ __all__ = [
     "lib", "lib_path", "rope_apply", "bifocal_prefill", "bifocal_prefill_ie", "bifocal_decode",
     "bifocal_decode_batch", "workspace_bytes", "group_size", "Workspace", "BifocalError",
     "OP_PREFILL", "OP_DECODE", "OP_PREFILL_IE", "VARIANTS", "bifocal_prefill_variant",
-    "bifocal_decode_variant",
+    "bifocal_decode_variant", "bifocal_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libbifocal.so")
 
 OP_ROPE, OP_PREFILL, OP_DECODE, OP_PREFILL_IE = 0, 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 4 << 20  # BIFOCAL_NOALLOC_SCRATCH_BYTES
 VARIANTS = {"bifocal": 0, "interp": 1, "window": 2}
 _F32, _BF16 = 0, 1
 
@@ -59,6 +60,9 @@ def _load():
     lib.bifocal_decode_batch.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, f64, f32, i32, vp, sz, vp]
     lib.bifocal_decode_batch.restype = i32
+    lib.bifocal_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64,
+                                           f32, i32, vp]
+    lib.bifocal_decode_noalloc.restype = i32
     lib.bifocal_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32]
     lib.bifocal_workspace_bytes.restype = sz
     lib.bifocal_status_string.argtypes = [i32]
@@ -373,4 +377,28 @@ def bifocal_decode_variant(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.
             _dev(lse, "lse") if lse is not None else 0, ctypes.cast(pos_arr, ctypes.c_void_p),
             B, S, Hq, Hkv, D, int(w0), int(w_pretrained), float(theta), float(softmax_scale),
             code, _dtype_code(q), ws.ptr, ws.nbytes, _stream(stream)), "bifocal_decode_variant")
+    return out, lse
+
+
+def bifocal_decode_noalloc(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, pos: int,
+                           w0: int, w_pretrained: int, theta: float, softmax_scale: float = 0.0,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           want_lse: bool = True, stream=None
+                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """bifocal_decode without a workspace (bf16, D = 128): the library keeps the split
+    partials in a fixed device array of its own per GPU; calls that overlap on one GPU
+    race.  Pass out (and lse) to allocate nothing here either."""
+    if q.dim() != 2 or Kcache.dim() != 3 or Vcache.shape != Kcache.shape:
+        raise BifocalError("expected q [Hq,D], Kcache and Vcache [S,Hkv,D]")
+    Hq, D = q.shape
+    S, Hkv = Kcache.shape[0], Kcache.shape[1]
+    if pos + 1 > S:
+        raise BifocalError("the cache holds fewer than pos + 1 entries")
+    _same(q, Kcache, Vcache)
+    out, lse = _outputs(q, out, lse, want_lse, (Hq,))
+    _check(lib().bifocal_decode_noalloc(
+        _dev(q, "q"), _dev(Kcache, "Kcache"), _dev(Vcache, "Vcache"), _dev(out, "out"),
+        _dev(lse, "lse") if lse is not None else 0, int(pos), Hq, Hkv, D, int(w0),
+        int(w_pretrained), float(theta), float(softmax_scale), _dtype_code(q), _stream(stream)),
+        "bifocal_decode_noalloc")
     return out, lse

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libbifocal.so")
 SOURCES = ["api.cpp", "tables.hip", "rope.hip", "decode.hip", "decode_mfma.hip",
-           "prefill_f32.hip", "prefill_mfma.hip", "prefill_ie.hip"]
+           "prefill_f32.hip", "prefill_mfma.hip", "prefill_ie.hip", "noalloc.hip"]
 ARCH = os.environ.get("BIFOCAL_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -264,12 +264,16 @@ bf_status bifocal_prefill_ie(const void* Q, const void* K, const void* V, void* 
 
 namespace {
 
-// Shared by bifocal_decode (one sequence) and bifocal_decode_batch.
+// Shared by bifocal_decode (one sequence), bifocal_decode_batch and the variants.  With
+// fixed_part set (the no-allocation entry point), the matrix-core path keeps its partials
+// there (fixed_part_bytes of room) instead of in a workspace, and other paths are refused.
 bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, void* o, float* lse,
                       const int32_t* pos, int32_t B, int64_t S, int32_t Hq, int32_t Hkv,
                       int32_t D, int32_t w0, int32_t w_pretrained, double theta,
                       float softmax_scale, bf_dtype dt, void* ws, size_t ws_bytes,
-                      bf_stream stream, int32_t variant = BF_VARIANT_BIFOCAL) {
+                      bf_stream stream, int32_t variant = BF_VARIANT_BIFOCAL,
+                      float* fixed_part = nullptr, size_t fixed_part_bytes = 0,
+                      bool validate_only = false) {
   if (B < 0 || (B > 0 && (!q || !Kcache || !Vcache || !o || !pos)) || S < 1 || Hq < 1 ||
       Hkv < 1 || Hq % Hkv || w0 < 1 || w_pretrained < 1 || !(theta > 0.0) ||
       !std::isfinite(theta) || !std::isfinite(softmax_scale))
@@ -291,9 +295,19 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
     return BF_EINVAL;
   const int32_t n_keys = max_pos + 1;
   if (n_keys >= kMaxPositions) return BF_EUNSUPPORTED;
-  if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
-  const WsLayout lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes, 0, B);
-  if (lay.scratch_off == 0 || lay.n_cap < n_keys) return BF_EWORKSPACE;
+  const size_t part_row = (size_t)(D + 2) * sizeof(float);  // one partial
+  WsLayout lay{};
+  if (fixed_part || validate_only) {
+    if (dt != BF_BF16 || D != 128) return BF_EUNSUPPORTED;
+    // at least one partial per (sequence, query head) of a launch must fit
+    if ((size_t)std::min<int32_t>(B, kDecodeMaxBatch) * Hq * part_row > fixed_part_bytes)
+      return BF_EWORKSPACE;
+  } else {
+    if (!ws || !aligned(ws, 256)) return BF_EWORKSPACE;
+    lay = ws_layout(BF_OP_DECODE, Hq, Hkv, D, ws_bytes, 0, B);
+    if (lay.scratch_off == 0 || lay.n_cap < n_keys) return BF_EWORKSPACE;
+  }
+  if (validate_only) return BF_OK;
 
   hipStream_t st = (hipStream_t)stream;
   char* wsb = reinterpret_cast<char*>(ws);
@@ -310,7 +324,7 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
     a.q = q;
     a.K = Kcache;
     a.V = Vcache;
-    a.part = reinterpret_cast<float*>(wsb + lay.scratch_off);
+    a.part = fixed_part ? fixed_part : reinterpret_cast<float*>(wsb + lay.scratch_off);
     a.o = o;
     a.lse = lse;
     a.seq_stride = seq_stride;
@@ -320,7 +334,7 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
     a.w0 = w0;
     a.scale_log2 = scale_log2;
     a.variant = variant;
-    a.hdr = reinterpret_cast<TableHeader*>(ws);
+    a.hdr = fixed_part ? nullptr : reinterpret_cast<TableHeader*>(ws);
     a.n_cap = lay.n_cap;
     for (int32_t b0 = 0; b0 < B; b0 += kDecodeMaxBatch) {
       const int nb = std::min<int32_t>(kDecodeMaxBatch, B - b0);
@@ -332,6 +346,9 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
       int64_t nwg = (512 + (int64_t)nb * Hkv - 1) / ((int64_t)nb * Hkv);
       nwg = std::min<int64_t>(nwg, std::max<int64_t>(1, nblk / (4 * 8)));
       nwg = std::max<int64_t>(1, std::min<int64_t>(nwg, kDecodeMaxParts));
+      if (fixed_part)  // fewer splits when the fixed buffer holds fewer partials
+        nwg = std::max<int64_t>(
+            1, std::min<int64_t>(nwg, (int64_t)(fixed_part_bytes / ((size_t)nb * Hq * part_row))));
       a.b_base = b0;
       a.nseq = nb;
       a.nwg = (int32_t)nwg;
@@ -346,6 +363,7 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
     return BF_OK;
   }
 
+  if (fixed_part) return BF_EUNSUPPORTED;  // unreachable: checked above
   // Vector path: one split launch + combine per sequence, sharing the table and the
   // partials buffer (stream order).
   bf_status s = ensure_table(ws, lay, D, theta, n_keys, st);
@@ -384,6 +402,22 @@ bf_status decode_impl(const void* q, const void* Kcache, const void* Vcache, voi
 }
 
 }  // namespace
+
+namespace bifocal {
+// bifocal_decode with its partials in a caller-given device buffer (no workspace).  With
+// part = null, only the argument checks run (no HIP call): the status they return.
+bf_status decode_fixed_partials(const void* q, const void* Kcache, const void* Vcache, void* o,
+                                float* lse, int32_t pos, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t w0, int32_t w_pretrained, double theta,
+                                float softmax_scale, bf_dtype dt, float* part, size_t part_bytes,
+                                bf_stream stream) {
+  if (pos < 0 || pos == INT32_MAX) return BF_EINVAL;
+  return decode_impl(q, Kcache, Vcache, o, lse, &pos, 1, (int64_t)pos + 1, Hq, Hkv, D, w0,
+                     w_pretrained, theta, softmax_scale, dt, nullptr, 0, stream,
+                     BF_VARIANT_BIFOCAL, part, part ? part_bytes : BIFOCAL_NOALLOC_SCRATCH_BYTES,
+                     part == nullptr);
+}
+}  // namespace bifocal
 
 extern "C" {
 

@@ -51,7 +51,8 @@ struct DecodeBatchArgs {
   int32_t variant;          // kVariant*
   // The workspace's position-table header and the rows the table region holds in this
   // call's layout: the partials sit past them and may overwrite rows a larger earlier
-  // table held, so the kernel lowers the header's row count to n_cap.
+  // table held, so the kernel lowers the header's row count to n_cap (hdr null: the
+  // partials are not in a workspace).
   TableHeader* hdr;
   int32_t n_cap;
   DecSeq seq[kDecodeMaxBatch];

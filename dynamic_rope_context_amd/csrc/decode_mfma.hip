@@ -114,7 +114,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, kq = lane >> 4;  // MFMA column / row, K group
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (a.hdr && blockIdx.x == 0 && threadIdx.x == 0) {
     // table rows past this layout's capacity are overwritten by the partials below:
     // a later prefill on the same workspace must not trust them
     volatile TableHeader* h = a.hdr;

@@ -226,6 +226,27 @@ bf_status bifocal_decode_variant(const void* q, const void* Kcache, const void* 
                                  void* ws, size_t ws_bytes, bf_stream stream);
 
 /*
+ * bifocal_decode_noalloc -- bifocal_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument, nothing allocated, freed or synchronised.
+ *   The split partials live in a device array of BIFOCAL_NOALLOC_SCRATCH_BYTES that the
+ *   library holds on each GPU it runs on until the process ends (its address is looked up
+ *   on the first call on a device).  Every call on a GPU shares that array: calls that
+ *   overlap on one GPU race; calls ordered on one stream are safe.
+ *   Arguments, layouts and results as for bifocal_decode, on the matrix-core path only:
+ *   dt = BF_BF16 and D = 128 (BF_EUNSUPPORTED otherwise).  When the array holds fewer
+ *   partials than the usual split count wants (Hq above about 64), the step uses fewer
+ *   splits; BF_EWORKSPACE if even one partial per query head does not fit.  stream must
+ *   belong to the current device (BF_EINVAL otherwise); BF_EHIP if the array's address
+ *   cannot be found.
+ */
+#define BIFOCAL_NOALLOC_SCRATCH_BYTES (4u << 20)
+bf_status bifocal_decode_noalloc(const void* q, const void* Kcache, const void* Vcache, void* o,
+                                 float* lse, int32_t pos, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t w0, int32_t w_pretrained, double theta,
+                                 float softmax_scale, bf_dtype dt, bf_stream stream);
+
+/*
  * bifocal_workspace_bytes -- workspace size for an operation.
  *   max_len: the longest sequence a prefill will see, or the largest pos + 1 for decode.
  *   total_tokens, num_seqs: prefill (both ops): the largest T and B of the calls that will use the

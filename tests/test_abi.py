@@ -16,6 +16,7 @@ BF_OK, BF_EINVAL, BF_EUNSUPPORTED, BF_EWORKSPACE = 0, 1, 2, 3
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)
     return sorted(set(re.findall(r"\b(\w+)\s*\(", text)) - {"defined", "if", "sizeof"})
 
 
@@ -31,7 +32,8 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("bifocal_prefill", "bifocal_decode", "rope_apply", "bifocal_workspace_bytes",
               "bifocal_status_string", "bifocal_group_size", "bifocal_prefill_ie",
-              "bifocal_decode_batch", "bifocal_prefill_variant", "bifocal_decode_variant"):
+              "bifocal_decode_batch", "bifocal_prefill_variant", "bifocal_decode_variant",
+              "bifocal_decode_noalloc"):
         assert n in names
 
 
@@ -148,6 +150,29 @@ def test_decode_rejects_bad_arguments_before_launch(lib):
     assert _decode(lib, K=24) == BF_EINVAL
     assert _decode(lib, ws=0) == BF_EWORKSPACE
     assert _decode(lib, ws_bytes=1 << 12) == BF_EWORKSPACE
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(q=16, K=16, V=16, o=16, lse=0, pos=100, Hq=4, Hkv=1, D=128, w0=4, w_pre=16,
+             theta=1e4, scale=0.0, dt=1)
+    a.update(kw)
+    return lib.bifocal_decode_noalloc(a["q"], a["K"], a["V"], a["o"], a["lse"], a["pos"],
+                                      a["Hq"], a["Hkv"], a["D"], a["w0"], a["w_pre"], a["theta"],
+                                      a["scale"], a["dt"], None)
+
+
+def test_decode_noalloc_rejects_bad_arguments_before_any_hip_call(lib):
+    # the checks run before the device lookup, so they work without a GPU
+    assert _decode_noalloc(lib, pos=-1) == BF_EINVAL
+    assert _decode_noalloc(lib, q=0) == BF_EINVAL
+    assert _decode_noalloc(lib, w0=0) == BF_EINVAL
+    assert _decode_noalloc(lib, Hq=6, Hkv=4) == BF_EINVAL
+    assert _decode_noalloc(lib, Hq=12, Hkv=4) == BF_EUNSUPPORTED
+    assert _decode_noalloc(lib, D=64) == BF_EUNSUPPORTED       # matrix-core path only
+    assert _decode_noalloc(lib, dt=0) == BF_EUNSUPPORTED       # bf16 only
+    assert _decode_noalloc(lib, K=24) == BF_EINVAL
+    # one partial per query head must fit the fixed array
+    assert _decode_noalloc(lib, Hq=8192, Hkv=1024) == BF_EWORKSPACE
 
 
 def _decode_batch(lib, **kw):
