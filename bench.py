@@ -147,19 +147,21 @@ def prefill_flops(seqlens, w0, Hq, D):
     return 4 * D * Hq * pc + 2 * D * Hq * pw, 4 * D * Hq * pc
 
 
-def bench_prefill(bf, torch, W, steps, warmup, w0=None, three_pass=False):
+def bench_prefill(bf, torch, W, steps, warmup, w0=None, three_pass=False,
+                  name="qwen3_4b_128k"):
     """w0 overrides the window (w0 >= L: vanilla mode, every pair local); three_pass
     times the literal inclusion-exclusion form (three passes + LSE merge)."""
-    w = W.get("qwen3_4b_128k")
+    w = W.get(name)
     if w0 is not None:
         import dataclasses
         w = dataclasses.replace(w, w0=w0)
     T = w.total_tokens
     q, k, v = W.raw_inputs_torch(w, "cuda")
-    # standard RoPE at absolute positions, built with the library's own rope_apply
-    bf.rope_apply(q, w.theta)
-    bf.rope_apply(k, w.theta)
+    # standard RoPE at each sequence's positions, built with the library's own rope_apply
     cu = [int(c) for c in w.cu_seqlens]
+    for b in range(len(cu) - 1):
+        bf.rope_apply(q[cu[b]:cu[b + 1]], w.theta)
+        bf.rope_apply(k[cu[b]:cu[b + 1]], w.theta)
     out = torch.empty_like(q)
     lse = torch.empty((w.Hq, T), dtype=torch.float32, device="cuda")
     op = bf.OP_PREFILL_IE if three_pass else bf.OP_PREFILL
@@ -184,6 +186,50 @@ def bench_prefill(bf, torch, W, steps, warmup, w0=None, three_pass=False):
     F, Fc = prefill_flops(w.seqlens, w.w0, w.Hq, w.D)
     assert bool(torch.isfinite(out).all())
     return w, ms, F, Fc, float(np.median(per_call))
+
+
+def bench_other_prefills(bf, torch, W, steps, warmup):
+    """The Qwen3-1.7B 32K layer (G = 1: every pair local) and the Qwen3-8B ragged layer
+    (two sequences, G = 4 and 2) on the GPU: time per call, counted TFLOP/s (the same F
+    definition as the headline) and its fraction of the bf16 dense peak."""
+    out = {}
+    for name in ("qwen3_1p7b_32k_g1", "qwen3_8b_ragged"):
+        log(f"prefill: {name}")
+        w, ms, F, Fc, ms_med = bench_prefill(bf, torch, W, steps, warmup, name=name)
+        tf = F / (ms * 1e-3) / 1e12
+        out[name] = {"seqlens": list(w.seqlens), "ms_per_call": round(ms, 4),
+                     "ms_median": round(ms_med, 4), "flops_per_call": F,
+                     "tflops": round(tf, 3), "causal_tflops": round(Fc / (ms * 1e-3) / 1e12, 3),
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"prefill {name}: {ms:.3f} ms/call, {tf:.1f} TFLOP/s counted")
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_rope_apply(bf, torch, W, steps, warmup):
+    """rope_apply in place on the 128K workload's query tensor [131072, 32, 128] bf16:
+    every element read and written once, against the HBM peak."""
+    w = W.get("qwen3_4b_128k")
+    x = torch.randn((w.total_tokens, w.Hq, w.D), device="cuda").to(torch.bfloat16)
+    for _ in range(warmup):
+        bf.rope_apply(x, w.theta)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with quiet_host():
+        e0.record(stream)
+        for _ in range(steps):
+            bf.rope_apply(x, w.theta)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    nbytes = 2.0 * x.numel() * x.element_size()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del x
+    torch.cuda.empty_cache()
+    return {"tensor": [w.total_tokens, w.Hq, w.D], "dtype": "bf16", "us_per_call": round(us, 2),
+            "bytes_per_call": nbytes, "GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def bench_decode(bf, torch, W, passes, warmup, w0=None):
@@ -410,6 +456,9 @@ def main():
                     help="skip the three-pass inclusion-exclusion comparison run")
     ap.add_argument("--no-decode-batch", action="store_true",
                     help="skip the batched decode run (8 sequences x 16K rows)")
+    ap.add_argument("--no-other-prefills", action="store_true",
+                    help="skip the 32K (G = 1) and ragged prefill workloads")
+    ap.add_argument("--no-rope", action="store_true", help="skip the rope_apply run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -489,6 +538,12 @@ def main():
                            "dtype": "bf16", "data": "synthetic",
                            "config": {"workload": "qwen3_8b_decode_128k"},
                            "roofline": dec["roofline"], "decode_batch": dec.get("batch")})
+    if not args.no_other_prefills and args.only in ("all", "prefill"):
+        result["other_prefills"] = bench_other_prefills(bf, torch, W, args.steps, args.warmup)
+    if not args.no_rope and args.only in ("all", "prefill"):
+        log("rope_apply: 128K query tensor")
+        result["rope_apply"] = bench_rope_apply(bf, torch, W, args.steps, args.warmup)
+        log(f"rope_apply: {result['rope_apply']}")
     if not args.no_three_pass and args.only in ("all", "prefill"):
         log("three-pass prefill: qwen3_4b_128k, passes A, B, C + merge")
         _, tms, _, _, _ = bench_prefill(bf, torch, W, args.steps, args.warmup, three_pass=True)

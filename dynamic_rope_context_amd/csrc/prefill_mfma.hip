@@ -122,55 +122,121 @@ __device__ __forceinline__ int fp16_range_exp(float m) {
   return (x - 29) >> 1;
 }
 
-// Per KV head: the top kSelPairs pairs by the bound max|k_m| * max_h |q_{h,m}| (squared),
-// and the operand exponents of the group's remote queries, remote keys and values.
+// Argmax over the 64 lanes of a wave (lane = RoPE pair); the lowest pair wins a tie.
+__device__ __forceinline__ void wave_argmax(float v, int& bi, float& bv) {
+  bv = v;
+  bi = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+}
+
+// Per KV head (one wave, lane = RoPE pair m):
+//  * the kSelPairs pairs with the largest sum_h |q_h,m|^2 * |k_m|^2 (maxima over the
+//    tokens) get the hi/lo correction on both sides for every query head of the group
+//    (the key-tile records carry their key remainders): the sum ranks first the pairs
+//    that are large in the key, whose rounding errors reach every head;
+//  * then each query head r of the group in turn takes up to kHeadPairs of the remaining
+//    pairs with the largest |q_r,m|^2 * |k_m|^2 for a query-side correction (its query
+//    remainder against the fp16 key), laid out as slice r of a channel order that the
+//    remote key copies and query operands share (the other channels fill the free
+//    positions in increasing order);
+//  * the operand exponents of the group's remote queries, remote keys and values.
 __global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restrict__ mxq,
                                                          const uint32_t* __restrict__ mxk,
                                                          const uint32_t* __restrict__ mxv,
                                                          int Hq, int Hkv,
                                                          int32_t* __restrict__ sel) {
-  // one wave per KV head, lane = RoPE pair; kSelPairs rounds of a wave-wide argmax
-  // (the lowest pair wins a tie), each taking its winner out of the next rounds
+  __shared__ int s_slot[64];  // pair -> query head * kHeadPairs + slot, or -1
+  __shared__ uint8_t s_perm[128];
+  __shared__ bool s_used[128];
   const int g = blockIdx.x, m = threadIdx.x;
   const int rep = Hq / Hkv;
-  float q = 0.f;
-  for (int r = 0; r < rep; ++r) q = fmaxf(q, __uint_as_float(mxq[(g * rep + r) * 64 + m]));
+  int32_t* rec = sel + g * kSelStride;
+  float q = 0.f, qsum = 0.f;
+  for (int r = 0; r < rep; ++r) {
+    const float x = __uint_as_float(mxq[(g * rep + r) * 64 + m]);
+    q = fmaxf(q, x);
+    qsum += x;
+  }
   const float kk = __uint_as_float(mxk[g * 64 + m]);
   float vv = __uint_as_float(mxv[g * 64 + m]);
-  float bound = q * kk;  // >= 0
-  float qm = q, km = kk;
+  const float bound = qsum * kk;  // >= 0
+  bool taken = false;
   for (int p = 0; p < kSelPairs; ++p) {
-    float bv = bound;
-    int bi = m;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
+    int bi;
+    float bv;
+    wave_argmax(taken ? -1.f : bound, bi, bv);
+    if (m == 0) rec[p] = bi;
+    if (m == bi) taken = true;
+  }
+  int slot = -1;
+  for (int r = 0; r < rep; ++r) {
+    const float b = __uint_as_float(mxq[(g * rep + r) * 64 + m]) * kk;
+    for (int j = 0; j < kHeadPairs; ++j) {
+      int bi;
+      float bv;
+      wave_argmax(taken ? -1.f : b, bi, bv);
+      if (bv < 0.f) break;  // every pair taken (wave-uniform)
+      if (m == bi) {
+        taken = true;
+        slot = r * kHeadPairs + j;
       }
     }
-    if (m == 0) sel[g * kSelStride + p] = bi;
-    if (m == bi) bound = -1.f;
   }
+  s_slot[m] = slot;
+  float qm = q, km = kk;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     qm = fmaxf(qm, __shfl_xor(qm, o));
     km = fmaxf(km, __shfl_xor(km, o));
     vv = fmaxf(vv, __shfl_xor(vv, o));
   }
+  __syncthreads();
   if (m == 0) {
-    sel[g * kSelStride + kSelExpQ] = fp16_range_exp(qm);
-    sel[g * kSelStride + kSelExpK] = fp16_range_exp(km);
-    sel[g * kSelStride + kSelExpV] = fp16_range_exp(vv);
+    rec[kSelExpQ] = fp16_range_exp(qm);
+    rec[kSelExpK] = fp16_range_exp(km);
+    rec[kSelExpV] = fp16_range_exp(vv);
+    uint8_t* perm = s_perm;
+    bool* used = s_used;
+    uint32_t mask[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < 128; ++i) used[i] = false;
+    for (int pm = 0; pm < 64; ++pm) {
+      const int sl = s_slot[pm];
+      if (sl < 0) continue;
+      const int r = sl / kHeadPairs, j = sl % kHeadPairs;
+      perm[16 * r + j] = (uint8_t)pm;
+      perm[16 * r + 8 + j] = (uint8_t)(pm + 64);
+      used[16 * r + j] = used[16 * r + 8 + j] = true;
+      mask[r] |= (1u << j) | (1u << (8 + j));
+    }
+    int free_pos = 0;
+    for (int c = 0; c < 128; ++c) {
+      if (s_slot[c & 63] >= 0) continue;  // placed in its head's slice
+      while (used[free_pos]) ++free_pos;
+      perm[free_pos] = (uint8_t)c;
+      used[free_pos] = true;
+    }
+    for (int w = 0; w < 32; ++w)
+      rec[kSelPerm + w] = (int32_t)((uint32_t)perm[4 * w] | ((uint32_t)perm[4 * w + 1] << 8) |
+                                    ((uint32_t)perm[4 * w + 2] << 16) |
+                                    ((uint32_t)perm[4 * w + 3] << 24));
+    for (int r = 0; r < 8; ++r) rec[kSelMask + r] = (int32_t)mask[r];
   }
 }
 
 // ---------------------------------------------------------------------------
 // Key preparation: once per call, each key tile of each KV head is turned into the
 // record the main kernel copies into LDS verbatim (layout in prefill_args.h): the
-// remote copy R(f(j) - j) K_j 2^-e_k rounded to fp16, the hi/lo correction of the
+// remote copy R(f(j) - j) K_j 2^-e_k rounded to fp16, its channels in the KV head's
+// order from the pre-pass (slice r holds query head r's corrected pairs), the hi/lo
+// correction of the
 // selected pairs, and V^T 2^-e_v in fp16 (the PV operands are fp16: P keeps 11
 // significant bits instead of 8).  A key is rotated once here instead of once per query block that
 // reads it.  One workgroup (256 threads) per (tile, KV head).
@@ -181,6 +247,8 @@ template <bool INTERP>
 __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
   using namespace mf;
   __shared__ __align__(16) uint16_t sv[BK][D + 8];
+  __shared__ __align__(16) float sy[BK][D + 4];  // rotated keys, natural channel order
+  __shared__ uint8_t s_perm[D];
   __shared__ double s_invf[D / 2];  // theta_m (continuous remote positions only)
   const int g = blockIdx.y;
   const int t_local = blockIdx.x;
@@ -235,7 +303,6 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
   // G = 1 in the bifocal mode: every pair is local, the remote copy is never read (the
   // inclusion-exclusion passes read it whatever G is)
   if (G > 1 || args.mode != 0) {
-    uint4 y1p = zero, y2p = zero;
     if (valid) {
       const uint4 a = *reinterpret_cast<const uint4*>(Kp + row_off + 8 * p);
       const uint4 c = *reinterpret_cast<const uint4*>(Kp + row_off + 64 + 8 * p);
@@ -261,30 +328,42 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
         y1[e] *= ks;
         y2[e] *= ks;
       }
-      y1p = make_uint4(pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
-                       pack_f16(y1[6], y1[7]));
-      y2p = make_uint4(pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]), pack_f16(y2[4], y2[5]),
-                       pack_f16(y2[6], y2[7]));
+      float* r1 = &sy[k][8 * p];
+      float* r2 = &sy[k][64 + 8 * p];
+      *reinterpret_cast<float4*>(r1) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+      *reinterpret_cast<float4*>(r1 + 4) = make_float4(y1[4], y1[5], y1[6], y1[7]);
+      *reinterpret_cast<float4*>(r2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+      *reinterpret_cast<float4*>(r2 + 4) = make_float4(y2[4], y2[5], y2[6], y2[7]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        *reinterpret_cast<uint4*>(&sy[k][64 * q + 8 * p]) = zero;
+        *reinterpret_cast<uint4*>(&sy[k][64 * q + 8 * p + 4]) = zero;
+      }
     }
-    *reinterpret_cast<uint4*>(kr + k * D + 8 * p) = y1p;
-    *reinterpret_cast<uint4*>(kr + k * D + 64 + 8 * p) = y2p;
+    if (tid < 32) {  // the shared channel order of the remote operands, one byte each
+      const uint32_t w = (uint32_t)args.sel[g * kSelStride + kSelPerm + tid];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_perm[4 * tid + e] = (uint8_t)(w >> (8 * e));
+    }
+    __syncthreads();
+    // record position q of key k holds channel perm[q]
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        h[e] = pack_f16(sy[k][s_perm[64 * q + 8 * p + 2 * e]], sy[k][s_perm[64 * q + 8 * p + 2 * e + 1]]);
+      *reinterpret_cast<uint4*>(kr + k * D + 64 * q + 8 * p) = make_uint4(h[0], h[1], h[2], h[3]);
+    }
     if (tid < 4 * BK) {
       // hi/lo of selected pair cp of key ck: [lo ch0..7 | hi ch0..7], channel
       // q = pair (q % 4), component (q / 4)
       const int ck = tid >> 2, cp = tid & 3;
-      const int jc = kt * BK + ck;
-      uint32_t h1 = 0, l1 = 0, h2 = 0, l2 = 0;
-      if (jc < L) {
-        const int m = args.sel[g * kSelStride + cp];
-        const uint16_t* row = Kp + ((size_t)(start + jc) * Hkv + g) * D;
-        const float2 cs = interp ? angle_cs(jc * rpos, s_invf[m])
-                                 : tab[(size_t)(jc - alias_fast(jc, gdiv)) * 64 + m];
-        float z1, z2;
-        rot_neg(__uint_as_float((uint32_t)row[m] << 16), __uint_as_float((uint32_t)row[m + 64] << 16),
-                cs.x, cs.y, z1, z2);
-        split_f16(z1 * ks, h1, l1);
-        split_f16(z2 * ks, h2, l2);
-      }
+      const int m = args.sel[g * kSelStride + cp];
+      uint32_t h1, l1, h2, l2;  // zero past the sequence's end (staged zeros)
+      split_f16(sy[ck][m], h1, l1);
+      split_f16(sy[ck][m + 64], h2, l2);
       uint16_t* crow = kc + ck * 16;
       const int lo_at = 8 * ((ck >> 3) & 1), hi_at = 8 - lo_at;  // swizzled chunks
       crow[lo_at + cp] = (uint16_t)l1;
@@ -434,15 +513,27 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   auto vt_kt = [&](int v) __attribute__((always_inline)) { return v < nr ? r0 + v : ktA + (v - nr); };
 
   // ---- query operands -------------------------------------------------------------
-  // B operand of S^T = K Q^T: lane (column ln, half hf) holds channels 16s + 8hf + e.
-  u32x4 qop[8];   // remote pass: fp16 of R(f(i)-i) q; local pass: bf16 q
-  u32x4 qcor;     // hi (half 0) or lo (half 1) of the 8 selected remote channels
+  // B operand of S^T = K Q^T: lane (column ln, half hf) holds operand positions
+  // 16s + 8hf + e.  Local pass: the bf16 query, channel = position.  Remote pass: the fp16
+  // of R(f(i)-i) q 2^-e_q with the channels in the KV head's order from the pre-pass
+  // (position p holds channel perm[p], the order of the remote key copies), so that slice
+  // hr holds the pairs chosen for this wave's query head.
+  u32x4 qop[8];
+  u32x4 qcor;     // hi (half 0) or lo (half 1) of the 8 channels of the both-sided pairs
+  u32x4 qcorh;    // fp16 remainders of slice hr (zero at positions without a chosen pair)
+  const int hr = wave / PBLK;  // this wave's query head within the group
   auto load_q_std = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
   };
   const float qs = __builtin_ldexpf(1.f, -args.sel[g * kSelStride + kSelExpQ]);
+  // Runs before any transfer into the LDS ring, whose space holds the rotated rows of
+  // each wave meanwhile (natural channel order, float32) for the gather into the channel
+  // order; the workgroup meets twice.
+  __shared__ uint8_t s_qperm[D];
   auto load_q_remote = [&]() __attribute__((always_inline)) {
+    constexpr int QS_LD = D + 4;  // floats per staged row
+    float* stg = reinterpret_cast<float*>(smem_raw) + wave * (32 * QS_LD) + ln * QS_LD;
     const int n = qrow_i - alias_fast(qrow_i, gdiv);
     uint4 raw[8];
 #pragma unroll
@@ -459,28 +550,52 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         y1[e] *= qs;
         y2[e] *= qs;
       }
-      qop[s] = u32x4{pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
-                     pack_f16(y1[6], y1[7])};
-      qop[s + 4] = u32x4{pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]), pack_f16(y2[4], y2[5]),
-                         pack_f16(y2[6], y2[7])};
+      float* r1 = stg + 16 * s + 8 * hf;
+      float* r2 = r1 + 64;
+      *reinterpret_cast<float4*>(r1) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+      *reinterpret_cast<float4*>(r1 + 4) = make_float4(y1[4], y1[5], y1[6], y1[7]);
+      *reinterpret_cast<float4*>(r2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+      *reinterpret_cast<float4*>(r2 + 4) = make_float4(y2[4], y2[5], y2[6], y2[7]);
+    }
+    if (tid < 32) {
+      const uint32_t w = (uint32_t)args.sel[g * kSelStride + kSelPerm + tid];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_qperm[4 * tid + e] = (uint8_t)(w >> (8 * e));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w4[e] = pack_f16(stg[s_qperm[16 * s + 8 * hf + 2 * e]], stg[s_qperm[16 * s + 8 * hf + 2 * e + 1]]);
+      qop[s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
+    {
+      const uint32_t mask = (uint32_t)args.sel[g * kSelStride + kSelMask + hr] >> (8 * hf);
+      uint32_t lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t h;
+        split_f16(stg[s_qperm[16 * hr + 8 * hf + e]], h, lo[e]);
+        if (!((mask >> e) & 1u)) lo[e] = 0u;
+      }
+      qcorh = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
+                    lo[6] | (lo[7] << 16)};
     }
     uint32_t part[8];
 #pragma unroll
     for (int p = 0; p < kSelPairs; ++p) {
       const int m = args.sel[g * kSelStride + p];
-      const float x1 = __uint_as_float((uint32_t)qrow[m] << 16);
-      const float x2 = __uint_as_float((uint32_t)qrow[m + 64] << 16);
-      const float2 cs = interp ? angle_cs(qrow_i * rpos, s_invf[m]) : trow[m];
-      float y1, y2;
-      rot_neg(x1, x2, cs.x, cs.y, y1, y2);
       uint32_t h1, l1, h2, l2;
-      split_f16(y1 * qs, h1, l1);
-      split_f16(y2 * qs, h2, l2);
+      split_f16(stg[m], h1, l1);
+      split_f16(stg[m + 64], h2, l2);
       part[p] = hf ? l1 : h1;
       part[p + 4] = hf ? l2 : h2;
     }
     qcor = u32x4{part[0] | (part[1] << 16), part[2] | (part[3] << 16),
                  part[4] | (part[5] << 16), part[6] | (part[7] << 16)};
+    __syncthreads();  // every wave has read its rows before the ring is refilled
   };
 
   // ---- staging: LDS-DMA straight from the key-tile records / K rows ----------------
@@ -550,7 +665,9 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     for (int s = 0; s < 8; ++s)
       sacc = mfma_f16(*reinterpret_cast<const u32x4*>(krow + 16 * s), qop[s], sacc);
     const uint16_t* crow = st.kc + ln * KC_LD + 8 * (hf ^ ((ln >> 3) & 1));
-    return mfma_f16(*reinterpret_cast<const u32x4*>(crow), qcor, sacc);
+    sacc = mfma_f16(*reinterpret_cast<const u32x4*>(crow), qcor, sacc);
+    // query-side remainders of this head's pairs against the fp16 keys of slice hr
+    return mfma_f16(*reinterpret_cast<const u32x4*>(krow + 16 * hr), qcorh, sacc);
   };
   auto qk_local = [&](int so) __attribute__((always_inline)) -> f32x16 {
     const Stage& st = *reinterpret_cast<const Stage*>(smem_raw + so);

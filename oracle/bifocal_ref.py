@@ -57,7 +57,9 @@ matrices on tiny inputs; the three-pass inclusion-exclusion identity; G = 1
 equals vanilla causal RoPE attention (torch SDPA, float64); w0 = 1 equals pure
 aliased attention (torch SDPA on aliased rotations); every remote angle stays
 on the pretrained grid; rotations compose additively; RoPE against a
-complex-number formulation; decode equals the last prefill row.
+complex-number formulation; decode equals the last prefill row; the table reference
+(``rope_tables_ref``, both column pairs) against RoPE applied to unit vectors, with the
+correction columns composing with the standard ones to the aliased angle.
 
 Parity unpinned where the pages fix nothing: they print no worked numeric example,
 so the readings above (rotate-half pairing, the sliding window, query offset 0) are

@@ -43,13 +43,17 @@ class Scheme:
 
     pairs: RoPE pairs per KV head whose fp16 remainders enter the remote scores on both
       sides (hi*lo + lo*hi), chosen from max_h |q_h|^2 * max |k|^2 over the group.
-    q_pairs: further pairs per query head (chosen from that head's |q_h|^2 * |k|^2)
-      whose query remainder enters against the key's fp16 value (lo*hi only).
+    q_pairs: pairs per query head (chosen from that head's max |q_h|^2 * max |k|^2) whose
+      query remainder enters against the key's fp16 value (lo*hi only).
+    k_only: the per-KV-head pairs give only the key remainder against the query's fp16
+      value (hi*lo), their query side is left to q_pairs.
     p_type: "bf16" or "f16", the type of P in the PV product and in the row sum.
     """
     pairs: int = 4
     p_type: str = "bf16"
     q_pairs: int = 0
+    k_only: bool = False     # the per-KV-head pairs correct the key side only (lo of k)
+    kv_sum: bool = False     # per-KV-head pairs by sum_h |q_h|^2 * |k|^2 instead of max_h
 
 def _f32(x):
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
@@ -98,29 +102,35 @@ def _top(bound, n: int, exclude=()):
     return order[:n]
 
 
-def select_pairs(Q, K, npairs: int):
-    """Per KV head, the npairs RoPE pairs with the largest max_h |q|^2 * max |k|^2 (pair
-    squared norms in float32 over all tokens of the call), ties to the lower pair.
-    Returns [Hkv, npairs] pair indices."""
+def select_pairs(Q, K, npairs: int, by_sum: bool = False):
+    """Per KV head, the npairs RoPE pairs with the largest max_h |q_h|^2 * max |k|^2, or
+    with by_sum the largest sum_h max |q_h|^2 * max |k|^2 (pair squared norms in float32
+    over all tokens of the call), ties to the lower pair.  Returns [Hkv, npairs]."""
     mq, mk = pair_bounds(Q, K)
     Hq, Hkv = mq.shape[0], mk.shape[0]
     rep = Hq // Hkv
     out = np.zeros((Hkv, npairs), dtype=np.int64)
     for g in range(Hkv):
-        out[g] = _top(mq[g * rep:(g + 1) * rep].max(axis=0) * mk[g], npairs)
+        qq = mq[g * rep:(g + 1) * rep]
+        out[g] = _top((qq.sum(axis=0) if by_sum else qq.max(axis=0)) * mk[g], npairs)
     return out
 
 
-def select_query_pairs(Q, K, kv_pairs, nq: int):
-    """Per query head, nq further pairs (not among its KV head's kv_pairs) with the largest
-    max |q_h|^2 * max |k|^2.  Returns [Hq, nq]."""
+def select_query_pairs(Q, K, kv_pairs, nq: int, exclude_kv: bool = True):
+    """Per query head, up to nq pairs with the largest max |q_h|^2 * max |k|^2, not among
+    its KV head's kv_pairs (unless exclude_kv is false) and not taken by a lower query
+    head of the same group (heads in order; a pair sits in one head's set only).
+    Returns a list of Hq lists."""
     mq, mk = pair_bounds(Q, K)
     Hq, Hkv = mq.shape[0], mk.shape[0]
     rep = Hq // Hkv
-    out = np.zeros((Hq, nq), dtype=np.int64)
-    for hq in range(Hq):
-        g = hq // rep
-        out[hq] = _top(mq[hq] * mk[g], nq, exclude=set(int(m) for m in kv_pairs[g]))
+    out = []
+    for g in range(Hkv):
+        taken = set(int(m) for m in kv_pairs[g]) if exclude_kv else set()
+        for r in range(rep):
+            mine = _top(mq[g * rep + r] * mk[g], nq, exclude=taken)
+            taken.update(mine)
+            out.append(mine)
     return out
 
 
@@ -132,8 +142,34 @@ def _split_operands(y, sel_channels):
     return hi, lo
 
 
+def _online_softmax(s_rem, s_loc, remote, local, Vg, c2, p_round, nkt):
+    """The kernel's online softmax over the virtual tiles (remote pass over tiles 0..nkt-1,
+    then the local pass), vectorised: the lazy running max is a scan over the tile maxima,
+    and each tile's rounded probabilities are rescaled to the final max afterwards (the
+    kernel's running rescale, up to float32 rounding of the factors).  Returns the
+    unnormalised output [R, D], the row sum [R] and the final max [R]."""
+    R = s_rem.shape[0]
+    st = np.concatenate([np.where(remote, s_rem, -np.inf).reshape(R, nkt, BK),
+                         np.where(local, s_loc, -np.inf).reshape(R, nkt, BK)], axis=1)
+    valid = np.concatenate([remote.reshape(R, nkt, BK), local.reshape(R, nkt, BK)], axis=1)
+    mxc = _f32(st.max(axis=2) * c2)                      # [R, 2 nkt]; -inf on empty tiles
+    m = np.full(R, -1e30)
+    m_t = np.empty((R, 2 * nkt))
+    for t in range(2 * nkt):
+        cand = np.maximum(m, mxc[:, t])
+        m = np.where(cand > m + LAZY, cand, m)
+        m_t[:, t] = m
+    with np.errstate(invalid="ignore"):
+        p = np.where(valid, _f32(np.exp2(_f32(st * c2 - m_t[:, :, None]))), 0.0)
+    pr = p_round(p) * np.exp2(m_t - m[:, None])[:, :, None]  # to the final max
+    l = pr.sum(axis=(1, 2))
+    V2 = np.concatenate([Vg, Vg], axis=0)                  # keys of both passes
+    acc = pr.reshape(R, 2 * nkt * BK) @ V2
+    return acc, l, m
+
+
 def emulate_rows(Q, K, V, rows, w0: int, w_pretrained: int, theta: float, scheme: Scheme,
-                 pairs=None, q_pairs=None, scale=None):
+                 pairs=None, q_pairs=None, scale=None, row_block: int = 64):
     """O [R, Hq, D] (bf16 values) and LSE [R, Hq] of the kernel model at the given query
     rows of one sequence (Q, K, V: [L, H, D] float32 arrays of bf16 values, standard RoPE
     at positions 0 .. L-1).  pairs: [Hkv, n] selected pairs (default: select_pairs over
@@ -150,66 +186,50 @@ def emulate_rows(Q, K, V, rows, w0: int, w_pretrained: int, theta: float, scheme
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     c2 = float(np.float32(scale * 1.4426950408889634))
     if pairs is None:
-        pairs = select_pairs(Q, K, scheme.pairs) if scheme.pairs else np.zeros((Hkv, 0), int)
+        pairs = (select_pairs(Q, K, scheme.pairs, by_sum=scheme.kv_sum) if scheme.pairs
+                 else np.zeros((Hkv, 0), int))
     if q_pairs is None:
-        q_pairs = (select_query_pairs(Q, K, pairs, scheme.q_pairs) if scheme.q_pairs
-                   else np.zeros((Hq, 0), int))
-    jmax = int(rows.max()) + 1
-    nkt = (jmax + BK - 1) // BK
-    J = nkt * BK
-    pos = np.arange(J)
-    n_all = pos - pos // G
-    Kp = np.zeros((J, Hkv, D), dtype=np.float32)
-    Kp[:jmax] = K[:jmax]
-    Vp = np.zeros((J, Hkv, D))
-    Vp[:jmax] = V[:jmax]
-    k_rem = rotate_remote(Kp, n_all, theta)
-    q_rem = rotate_remote(Q[rows], rows - rows // G, theta)
+        q_pairs = (select_query_pairs(Q, K, pairs, scheme.q_pairs,
+                                      exclude_kv=not scheme.k_only) if scheme.q_pairs
+                   else [[] for _ in range(Hq)])
     p_round = _bf16 if scheme.p_type == "bf16" else _f16
     R = len(rows)
     O = np.zeros((R, Hq, D))
     LSE = np.zeros((R, Hq))
-    i = rows[:, None]
-    dist = i - pos[None, :]
-    causal = dist >= 0
-    local = causal & (dist < w0)
-    remote = causal & ~local
-    for g in range(Hkv):
-        selc = np.zeros(D, dtype=bool)
-        for m in pairs[g]:
-            selc[m] = selc[m + h] = True
-        kh, kl = _split_operands(k_rem[:, g, :], selc)
-        for r in range(rep):
-            hq = g * rep + r
-            selq = selc.copy()
-            for m in q_pairs[hq]:
-                selq[m] = selq[m + h] = True
-            qh, ql = _split_operands(q_rem[:, hq, :], selq)
-            s_rem = qh @ kh.T + qh @ kl.T + ql @ kh.T
-            s_loc = Q[rows, hq, :].astype(np.float64) @ Kp[:, g, :].astype(np.float64).T
-            s_rem, s_loc = _f32(s_rem), _f32(s_loc)
-            m = np.full(R, -1e30)
-            l = np.zeros(R)
-            acc = np.zeros((R, D))
-            for pass_mask, s in ((remote, s_rem), (local, s_loc)):
-                for t in range(nkt):
-                    sl = slice(t * BK, (t + 1) * BK)
-                    msk = pass_mask[:, sl]
-                    if not msk.any():
-                        continue
-                    st = np.where(msk, s[:, sl], -np.inf)
-                    mx = st.max(axis=1)
-                    cand = np.maximum(m, _f32(mx * c2))
-                    need = cand > m + LAZY
-                    mn = np.where(need, cand, m)
-                    f = _f32(np.exp2(m - mn))
-                    l = l * f
-                    acc = acc * f[:, None]
-                    m = mn
-                    p = np.where(msk, _f32(np.exp2(_f32(st * c2 - m[:, None]))), 0.0)
-                    pr = p_round(p)
-                    l = l + pr.sum(axis=1)
-                    acc = acc + pr @ Vp[sl, g, :]
-            O[:, hq, :] = _bf16(acc / l[:, None])
-            LSE[:, hq] = (m + np.log2(l)) * math.log(2.0)
+    order = np.argsort(rows)
+    for b0 in range(0, R, row_block):
+        idx = order[b0:b0 + row_block]
+        rb = rows[idx]
+        jmax = int(rb.max()) + 1
+        nkt = (jmax + BK - 1) // BK
+        J = nkt * BK
+        pos = np.arange(J)
+        Kp = np.zeros((J, Hkv, D), dtype=np.float32)
+        Kp[:jmax] = K[:jmax]
+        Vp = np.zeros((J, Hkv, D))
+        Vp[:jmax] = V[:jmax]
+        k_rem = rotate_remote(Kp, pos - pos // G, theta)
+        q_rem = rotate_remote(Q[rb], rb - rb // G, theta)
+        dist = rb[:, None] - pos[None, :]
+        causal = dist >= 0
+        local = causal & (dist < w0)
+        remote = causal & ~local
+        for g in range(Hkv):
+            selc = np.zeros(D, dtype=bool)
+            for m in pairs[g]:
+                selc[m] = selc[m + h] = True
+            kh, kl = _split_operands(k_rem[:, g, :], selc)
+            kstd = Kp[:, g, :].astype(np.float64)
+            for r in range(rep):
+                hq = g * rep + r
+                selq = np.zeros(D, dtype=bool) if scheme.k_only else selc.copy()
+                for m in q_pairs[hq]:
+                    selq[m] = selq[m + h] = True
+                qh, ql = _split_operands(q_rem[:, hq, :], selq)
+                s_rem = _f32(qh @ kh.T + qh @ kl.T + ql @ kh.T)
+                s_loc = _f32(Q[rb, hq, :].astype(np.float64) @ kstd.T)
+                acc, l, m = _online_softmax(s_rem, s_loc, remote, local, Vp[:, g, :], c2,
+                                            p_round, nkt)
+                O[idx, hq, :] = _bf16(acc / l[:, None])
+                LSE[idx, hq] = (m + np.log2(l)) * math.log(2.0)
     return O, LSE

@@ -71,12 +71,15 @@ def check_prefill(bf, w, Q, K, V, cu, tol, rows_per_seq=None):
 # rope_apply
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dt,G,use_pos", [("bf16", 1, False), ("bf16", 3, True),
-                                          ("f32", 1, True), ("f32", 4, False)])
-def test_rope_apply_matches_oracle(bf, dt, G, use_pos):
-    say(f"rope_apply dt={dt} G={G} pos_array={use_pos}")
+@pytest.mark.parametrize("dt,G,use_pos,D", [("bf16", 1, False, 128), ("bf16", 3, True, 128),
+                                            ("f32", 1, True, 128), ("f32", 4, False, 128),
+                                            ("bf16", 2, True, 64), ("bf16", 1, False, 100),
+                                            ("f32", 5, True, 36)])
+def test_rope_apply_matches_oracle(bf, dt, G, use_pos, D):
+    # D = 64, 128: 8-pair chunks with 16-byte accesses; D = 100, 36: one pair per thread
+    say(f"rope_apply dt={dt} G={G} pos_array={use_pos} D={D}")
     rng = np.random.default_rng(7)
-    T, H, D, theta = 300, 3, 128, 1e6
+    T, H, theta = 300, 3, 1e6
     x = to_dtype(rng.standard_normal((T, H, D)).astype(np.float32), dt)
     pos = rng.integers(0, 131072, size=T).astype(np.int32) if use_pos else None
     p = pos if use_pos else np.arange(T) + 1000
@@ -87,9 +90,14 @@ def test_rope_apply_matches_oracle(bf, dt, G, use_pos):
     got = host(xd).astype(np.float64)
     exact = rope_apply_ref(x, p, theta, G)
     if dt == "bf16":
-        # within one bf16 ulp of the exact value (float32 arithmetic, then one rounding)
+        # one bf16 rounding of a float32 rotation: within a bf16 ulp of the exact value,
+        # plus the float32 error of x1 c - x2 s, which is relative to the inputs and not
+        # to the result (it shows where the two products nearly cancel)
         ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
-        assert np.all(np.abs(got - exact) <= ulp)
+        x64 = x.astype(np.float64)
+        mag = np.abs(x64[..., :D // 2]) + np.abs(x64[..., D // 2:])
+        mag = np.concatenate([mag, mag], axis=-1)
+        assert np.all(np.abs(got - exact) <= ulp + 4 * 2.0 ** -24 * mag)
     else:
         mag = np.abs(x[..., :D // 2]).max() + np.abs(x[..., D // 2:]).max()
         assert np.max(np.abs(got - exact)) <= 4e-7 * mag
@@ -658,3 +666,38 @@ def test_prefill_decode_prefill_share_one_workspace(bf):
             e = errors(host(O)[rows], Or, lse.cpu().numpy()[:, rows].T, Lr)
         say(f"  step {step} ({'decode' if w_pre is None else f'prefill G={group_size(1500, w_pre)}'}): {e}")
         assert within(e, BF16_TOL), (step, e)
+
+
+def test_position_table_rows_match_reference(bf):
+    # The workspace keeps [256 B header][rows p: D/2 x (cos, sin) float32] after a call.
+    # Each entry must be the float64 value rounded once to float32 (at most one float32
+    # ulp off where the float64 result sits next to a rounding boundary), and read at
+    # n = x - f(x) with the sine negated it must give the correction rotation R(f(x) - x).
+    from oracle.bifocal_ref import rope_tables_ref
+    w = W.Workload("table", "prefill", "bf16", Hq=4, Hkv=2, D=128, w0=50, w_pretrained=700,
+                   theta=1e6, seqlens=(3000,), outliers=0, seed=41)
+    G = group_size(3000, w.w_pretrained)
+    Q, K, V, cu = prefill_inputs(w)
+    ws = bf.Workspace.for_op(bf.OP_PREFILL, 3000, w.Hq, w.Hkv, w.D, total_tokens=3000)
+    bf.bifocal_prefill(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), [0, 3000], w.w0,
+                       w.w_pretrained, w.theta, workspace=ws)
+    torch.cuda.synchronize()
+    off = ws.ptr - ws.buf.data_ptr()
+    raw = ws.buf[off:off + ws.nbytes].cpu().numpy()
+    magic = int(raw[:8].view(np.uint64)[0])
+    theta = float(raw[8:16].view(np.float64)[0])
+    D, n_valid = (int(x) for x in raw[16:24].view(np.int32))
+    say(f"  header: magic {magic:#x} theta {theta:g} D {D} rows {n_valid}")
+    assert theta == w.theta and D == 128 and n_valid >= 3000
+    tab = raw[256:256 + n_valid * 64 * 8].view(np.float32).reshape(n_valid, 64, 2)
+    c, s, cc, sc = rope_tables_ref(n_valid, 128, w.theta, G)
+    for got, want in ((tab[..., 0], c), (tab[..., 1], s)):
+        w32 = want.astype(np.float32)
+        ulp = np.spacing(np.abs(w32))
+        assert np.all(np.abs(got - w32) <= ulp)
+        assert np.mean(got == w32) >= 0.9999
+    x = np.arange(3000)
+    n = x - x // G
+    for got, want in ((tab[n, :, 0], cc[:3000]), (-tab[n, :, 1], sc[:3000])):
+        w32 = want.astype(np.float32)
+        assert np.all(np.abs(got - w32) <= np.spacing(np.abs(w32)))

@@ -157,11 +157,64 @@ def test_correction_rotation_composes_additively():
     direct = rope_complex(x, alias(pos, G), 1e6)
     # angles reach ~1.1e5 rad, where one float64 ulp of the angle is ~1.5e-11
     np.testing.assert_allclose(corrected, direct, rtol=0, atol=1e-10)
-    c, s, cc, sc = rope_tables_ref(100, D, 1e6, G)
-    for p in (0, 3, 4, 57, 99):
-        a = (p // G - p) * inv_freq(1e6, D)
-        np.testing.assert_allclose(cc[p], np.cos(a), atol=1e-15)
-        np.testing.assert_allclose(sc[p], np.sin(a), atol=1e-15)
+
+
+def _tables_from_unit_vectors(n_pos, D, theta, G):
+    """(cos, sin) columns read off RoPE (complex form) applied to the unit vectors e_m:
+    rotating e_m by angle a puts cos a in channel m and sin a in channel m + D/2."""
+    h = D // 2
+    eye = np.eye(D)[:h]                                    # e_0 .. e_{h-1}
+    p = np.arange(n_pos)
+    out = []
+    for pos in (p, p // G - p):                            # standard, correction
+        r = rope_complex(np.broadcast_to(eye, (n_pos, h, D)), pos, theta)  # [n, m, D]
+        out.append(r[:, np.arange(h), np.arange(h)])        # channel m of e_m's image
+        out.append(r[:, np.arange(h), np.arange(h) + h])    # channel m + D/2
+    return out
+
+
+@pytest.mark.parametrize("D,theta,G", [(64, 1e6, 4), (128, 1e4, 3), (8, 50.0, 1)])
+def test_rope_tables_match_rotated_unit_vectors(D, theta, G):
+    # the table generator's reference, both column pairs, against RoPE applied to unit
+    # vectors; the correction columns compose with the standard rotation to f(p)
+    n = 300
+    ref = rope_tables_ref(n, D, theta, G)
+    for got, want in zip(ref, _tables_from_unit_vectors(n, D, theta, G)):
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    c, s, cc, sc = ref
+    p = np.arange(n)
+    a_f = (p // G)[:, None] * inv_freq(theta, D)[None, :]
+    # R(f(p) - p) R(p) = R(f(p)): angle addition with the standard columns
+    np.testing.assert_allclose(cc * c - sc * s, np.cos(a_f), atol=1e-12)
+    np.testing.assert_allclose(sc * c + cc * s, np.sin(a_f), atol=1e-12)
+
+
+def test_rope_tables_d2_closed_form():
+    # D = 2, theta_0 = 1: the angles are the positions themselves
+    c, s, cc, sc = rope_tables_ref(10, 2, 1e4, 3)
+    for p in range(10):
+        assert abs(c[p, 0] - math.cos(p)) < 1e-15 and abs(s[p, 0] - math.sin(p)) < 1e-15
+        assert abs(cc[p, 0] - math.cos(p // 3 - p)) < 1e-15
+        assert abs(sc[p, 0] - math.sin(p // 3 - p)) < 1e-15
+
+
+@pytest.mark.parametrize("mistake", ["std_from_aliased", "correction_sign", "swap_cos_sin"])
+def test_rope_tables_planted_mistakes_are_caught(monkeypatch, mistake):
+    import oracle.bifocal_ref as ref
+    orig = ref.rope_tables_ref
+
+    def bad(n_pos, D, theta, G):
+        c, s, cc, sc = orig(n_pos, D, theta, G)
+        if mistake == "std_from_aliased":       # standard columns built from f(p)
+            a = (np.arange(n_pos) // G)[:, None] * inv_freq(theta, D)[None, :]
+            return np.cos(a), np.sin(a), cc, sc
+        if mistake == "correction_sign":        # R(p - f(p)) instead of R(f(p) - p)
+            return c, s, cc, -sc
+        return s, c, cc, sc                     # swap_cos_sin
+    monkeypatch.setattr(ref, "rope_tables_ref", bad)
+    monkeypatch.setitem(globals(), "rope_tables_ref", bad)
+    with pytest.raises(AssertionError):
+        test_rope_tables_match_rotated_unit_vectors(64, 1e6, 4)
 
 
 def test_rope_apply_ref_aliases_positions():

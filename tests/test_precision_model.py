@@ -5,12 +5,16 @@ query head and per KV head (the Qwen3-4B 128K and ragged workloads' layout), at
 GQA ratios 2 and 4.
 
 The bound checked is the LSE tolerance of the bf16 parity tests (5e-3) with margin: the
-scheme the kernel uses must stay at or below 3.5e-3 on the smoke workload and the many-
-short-sequences case, and at or below 4e-3 (80% of the bound) on every seed of the
-outlier layouts.  What remains is the fp16 rounding of every remote operand: an outlier
-channel (x8) makes both its query and its key rounding errors large (each is relative to
-the product |q_c k_c|), and at GQA ratio 4 a KV group carries up to 20 outlier pairs,
-beyond what a fixed set of corrected pairs covers cheaply.  The model is first
+scheme the kernel uses must stay at or below 4e-3 (80% of the bound) on every case.
+The scheme: fp16 remote operands and fp16 probabilities; the 4 RoPE pairs per KV head
+with the largest sum over the group's query heads of |q_h|^2 |k|^2 corrected on both
+sides (for every head); for each query head, 8 more pairs of its own corrected on the
+query side.  An outlier channel (x8) makes both rounding errors of its products large
+(each is relative to |q_c k_c|): the key outliers reach every head (both-sided set), a
+query outlier one head, whose query-side error is systematic over all keys (per-head
+set); its key-side error averages over the keys at long lengths.  At 128K (528 rows x 32
+heads of the Qwen3-4B workload, too slow for this suite) the model gives a worst LSE
+error of 2.5e-3, against 6.0e-3 for 4 both-sided pairs alone (which the kernel showed).  The model is first
 tied to the oracle (with every remote channel corrected and fp16 probabilities it must
 agree to a few 1e-4) and to the kernel's measured behaviour (the earlier scheme, bf16
 probabilities, must show the 4.9e-3 the kernel measured on the smoke workload)."""
@@ -22,11 +26,11 @@ from helpers import prefill_inputs
 from oracle.bifocal_ref import bifocal_rows
 from precision_model import Scheme, emulate_rows, select_pairs
 
-KERNEL = Scheme(pairs=4, p_type="f16")     # what the matrix-core prefill does
+KERNEL = Scheme(pairs=4, p_type="f16", q_pairs=8, kv_sum=True)  # the matrix-core prefill
+EARLIER_F16 = Scheme(pairs=4, p_type="f16")
 EARLIER = Scheme(pairs=4, p_type="bf16")   # bf16 probabilities
 EXACT = Scheme(pairs=64, p_type="f16")     # every remote channel corrected
-LSE_MARGIN = 3.5e-3
-LSE_MARGIN_LAYOUT = 4e-3
+LSE_MARGIN = 4e-3
 
 SMOKE = W.Workload("smoke", "prefill", "bf16", Hq=8, Hkv=2, D=128, w0=64, w_pretrained=256,
                    theta=1e6, seqlens=(1000, 77), outliers=4, seed=2024)
@@ -36,7 +40,7 @@ def _errors(w, scheme, n_uniform=None):
     """Worst (max |dO|, mean |dO|, max |dLSE|) of the model against the oracle over the
     sequences of w (all rows, or sampled rows)."""
     Q, K, V, cu = prefill_inputs(w)
-    pairs = select_pairs(Q, K, scheme.pairs)  # the pre-pass sees the whole packed call
+    pairs = select_pairs(Q, K, scheme.pairs, by_sum=scheme.kv_sum)  # over the whole call
     worst = [0.0, 0.0, 0.0]
     for b in range(len(cu) - 1):
         s0, s1 = int(cu[b]), int(cu[b + 1])
@@ -84,4 +88,4 @@ def test_kernel_scheme_on_workload_outlier_layout(rep, seed):
     w = W.Workload("layout", "prefill", "bf16", Hq=4 * rep, Hkv=4, D=128, w0=128,
                    w_pretrained=512, theta=1e6, seqlens=(2048,), outliers=4, seed=seed)
     mx, mean, lse = _errors(w, KERNEL, n_uniform=200)
-    assert lse <= LSE_MARGIN_LAYOUT and mx <= 2e-2 and mean <= 2e-3, (mx, mean, lse)
+    assert lse <= LSE_MARGIN and mx <= 2e-2 and mean <= 2e-3, (mx, mean, lse)
