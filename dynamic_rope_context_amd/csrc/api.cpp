@@ -167,6 +167,23 @@ bf_status prefill_impl(const void* Q, const void* K, const void* V, void* O, flo
     if (n == 0) continue;
     a.nseq = n;
     a.max_qblocks = maxq;
+    {
+      // levels of the matrix-core grid: sequences by query-block count, longest first
+      int ord[kMaxSeqPerLaunch], cnt[kMaxSeqPerLaunch];
+      for (int i = 0; i < n; ++i) {
+        ord[i] = i;
+        cnt[i] = (a.seq[i].len + rows - 1) / rows;
+      }
+      std::stable_sort(ord, ord + n, [&](int x, int y) { return cnt[x] > cnt[y]; });
+      a.nlvl = n;
+      a.lvl_start[0] = 0;
+      for (int k = 0; k < n; ++k) {
+        a.lvl_seq[k] = ord[k];
+        a.lvl_qb[k] = cnt[ord[k]];
+        const int next = k + 1 < n ? cnt[ord[k + 1]] : 0;
+        a.lvl_start[k + 1] = a.lvl_start[k] + (a.lvl_qb[k] - next) * (k + 1);
+      }
+    }
     if (!ie) {
       hipError_t e = dt == BF_BF16 ? launch_prefill_mfma(a, chunk_tiles, st)
                                    : launch_prefill_f32(a, st);

@@ -51,6 +51,16 @@ struct PrefillArgs {
   // frequency-interpolation variant of the pages' ablation)
   int32_t interp;
   SeqInfo seq[kMaxSeqPerLaunch];
+  // Query blocks of the matrix-core kernel, heaviest first across the launch's sequences
+  // and no workgroup without rows: with the sequences sorted by their query-block counts
+  // c_0 >= c_1 >= ... (c_n = 0), level k holds the blocks qb in [c_{k+1}, c_k) of the
+  // k + 1 longest sequences, qb descending, then sequence.  lvl_start[k] is the index of
+  // level k's first (sequence, block) pair, lvl_start[n] the number of pairs; lvl_qb[k] =
+  // c_k; lvl_seq[s] the launch-local index of the s-th longest sequence.
+  int32_t nlvl;
+  int32_t lvl_start[kMaxSeqPerLaunch + 1];
+  int32_t lvl_qb[kMaxSeqPerLaunch];
+  int32_t lvl_seq[kMaxSeqPerLaunch];
 };
 
 }  // namespace bifocal

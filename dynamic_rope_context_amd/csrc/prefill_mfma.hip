@@ -449,16 +449,18 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const int hf = lane >> 5;               // lane half
 
   // Workgroup -> (KV head, sequence, query block).  KV head is the fastest index so
-  // that the workgroups of one head share an XCD's L2; query blocks run longest-first.
+  // that the workgroups of one head share an XCD's L2; (sequence, block) pairs run
+  // heaviest-first over the launch's levels, and every workgroup has rows.
   const int Hkv = args.Hkv;
-  const int nseq = args.nseq;
   const int g = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
-  const int b = rest % nseq;
-  const int qb = args.max_qblocks - 1 - rest / nseq;
+  const int pid = blockIdx.x / Hkv;
+  int lv = 0;
+  while (lv + 1 < args.nlvl && args.lvl_start[lv + 1] <= pid) ++lv;
+  const int r_in = pid - args.lvl_start[lv];
+  const int qb = args.lvl_qb[lv] - 1 - r_in / (lv + 1);
+  const int b = args.lvl_seq[r_in % (lv + 1)];
   const int L = args.seq[b].len;
   const int i0 = qb * BMPOS;
-  if (i0 >= L) return;
   const int start = args.seq[b].start;
   const int G = args.seq[b].G;
   const DivMagic gdiv{args.seq[b].gmul, args.seq[b].gshift};
@@ -883,7 +885,7 @@ static hipError_t launch_mfma_rep(const PrefillArgs& args, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute((const void*)prefill_mfma_kernel<REP>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mf::kSmem);
   if (e != hipSuccess) return e;
-  const int blocks = args.Hkv * args.nseq * args.max_qblocks;
+  const int blocks = args.Hkv * args.lvl_start[args.nlvl];
   hipLaunchKernelGGL(prefill_mfma_kernel<REP>, dim3(blocks), dim3(512), mf::kSmem, stream, args);
   return hipGetLastError();
 }
