@@ -701,3 +701,31 @@ def test_position_table_rows_match_reference(bf):
     for got, want in ((tab[n, :, 0], cc[:3000]), (-tab[n, :, 1], sc[:3000])):
         w32 = want.astype(np.float32)
         assert np.all(np.abs(got - w32) <= np.spacing(np.abs(w32)))
+
+
+def test_decode_split_count_invariance(bf):
+    # The split count follows the launch: one sequence alone gets 39 workgroups per KV
+    # head here, the same sequence in a batch of eight gets 8.  Both results must meet the
+    # bf16 tolerance against the oracle and agree with each other within it.
+    w = W.Workload("splits", "decode", "bf16", Hq=32, Hkv=8, D=128, w0=256, w_pretrained=5000,
+                   theta=1e6, cache_len=20000, decode_steps=1, outliers=4, seed=515)
+    q_raw, Kc, Vc = decode_inputs(w)
+    pos = 19999
+    q = std_query(q_raw[0], pos, w.theta, "bf16")
+    qd, Kd, Vd = dev(q, "bf16"), dev(Kc, "bf16"), dev(Vc, "bf16")
+    o1, l1 = bf.bifocal_decode(qd, Kd, Vd, pos, w.w0, w.w_pretrained, w.theta)
+    B = 8
+    o8, l8 = bf.bifocal_decode_batch(qd.unsqueeze(0).expand(B, -1, -1).contiguous(),
+                                     Kd.unsqueeze(0).expand(B, -1, -1, -1).contiguous(),
+                                     Vd.unsqueeze(0).expand(B, -1, -1, -1).contiguous(),
+                                     [pos] * B, w.w0, w.w_pretrained, w.theta)
+    torch.cuda.synchronize()
+    Or, Lr = bifocal_decode_ref(q, Kc, Vc, pos, w.w0, w.w_pretrained, w.theta)
+    e1 = errors(host(o1), Or, l1.cpu().numpy(), Lr)
+    e8 = errors(host(o8[3]), Or, l8[3].cpu().numpy(), Lr)
+    d = errors(host(o1), host(o8[3]).astype(np.float64), l1.cpu().numpy(),
+               l8[3].cpu().numpy().astype(np.float64))
+    say(f"  alone {e1}; in a batch of 8 {e8}; between them {d}")
+    for e in (e1, e8, d):
+        assert within(e, BF16_TOL), e
+    assert all(torch.equal(o8[0], o8[b]) for b in range(1, B))
