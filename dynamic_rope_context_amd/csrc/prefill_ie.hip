@@ -1,11 +1,12 @@
 // Inclusion-exclusion merge of three attention passes (gfx950).
 //
-// Jet-Long technical summary, "Methodology" section 1: the pages compute the bifocal
-// attention as three FlashAttention passes whose LogSumExp statistics are merged so
-// that the remote window is not counted twice: A = local scores over the window
-// pairs, B = remote scores over all causal pairs, C = remote scores over the window
-// pairs, and Z = Z_B - Z_C + Z_A.  The fused kernels select each pair's rule instead;
-// this literal form exists to measure that fusion and to cross-check it on the GPU.
+// Jet-Long technical summary, "Methodology" section 2 (inference efficiency mechanisms):
+// the pages compute the bifocal attention as three FlashAttention passes whose
+// LogSumExp statistics are merged so that the remote window is not counted twice:
+// A = local scores over the window pairs, B = remote scores over all causal pairs,
+// C = remote scores over the window pairs, and Z = Z_B - Z_C + Z_A.  The fused kernels
+// select each pair's rule instead; this literal form exists to measure that fusion and
+// to cross-check it on the GPU.
 //
 // Per (token, head): m = max(LSE_A, LSE_B, LSE_C), w_x = exp(LSE_x - m),
 // z = w_B - w_C + w_A, O = (w_B O_B - w_C O_C + w_A O_A) / z, LSE = m + ln z.

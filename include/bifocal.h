@@ -139,8 +139,9 @@ bf_status bifocal_prefill_variant(const void* Q, const void* K, const void* V, v
 /*
  * bifocal_prefill_ie -- the same attention as bifocal_prefill, computed literally as
  * the pages' three passes merged by inclusion-exclusion of their LogSumExp statistics
- * (section 1): A = local scores over the window pairs (0 <= i - j < w0), B = remote
- * scores over all causal pairs, C = remote scores over the window pairs; then
+ * (section 2, inference efficiency): A = local scores over the window pairs
+ * (0 <= i - j < w0), B = remote scores over all causal pairs, C = remote scores over the
+ * window pairs; then
  *   Z = e^{LSE_B} - e^{LSE_C} + e^{LSE_A},
  *   O = (e^{LSE_B} O_B - e^{LSE_C} O_C + e^{LSE_A} O_A) / Z,   lse = ln Z.
  *   The passes run the bf16 matrix-core kernel in three modes and keep O_x in fp32;
