@@ -116,3 +116,33 @@ def test_graph_replays_match_eager(bf, what, dt, D):
         call()  # an eager call between replays
         torch.cuda.synchronize()
         assert torch.equal(out, o_ref), (what, "eager", r)
+
+
+def test_prefill_without_workspace_costs_no_more_than_with_one(bf):
+    # A call given no workspace allocates one (on the launch stream) and builds the
+    # position table in it: the table check runs on its full grid, so a fresh workspace
+    # costs one table build (tens of microseconds), not a serial rebuild.  At the 32K
+    # G = 1 layer shape each such call takes at most 1.1x a call on a ready workspace.
+    w = W.get("qwen3_1p7b_32k_g1")
+    q, k, v = W.raw_inputs_torch(w, "cuda")
+    bf.rope_apply(q, w.theta)
+    bf.rope_apply(k, w.theta)
+    cu = [0, w.total_tokens]
+    out = torch.empty_like(q)
+    ws = bf.Workspace.for_op(bf.OP_PREFILL, w.total_tokens, w.Hq, w.Hkv, w.D)
+    args = (q, k, v, cu, w.w0, w.w_pretrained, w.theta)
+
+    def timed(**kw):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bf.bifocal_prefill(*args, out=out, want_lse=False, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+    for _ in range(2):  # warm-up, including the allocator's first blocks of this size
+        timed(workspace=ws)
+        timed()
+    ref = min(timed(workspace=ws) for _ in range(3))
+    fresh = [timed() for _ in range(2)]
+    say(f"  with a workspace {ref:.3f} ms; without: {fresh}")
+    assert max(fresh) <= 1.1 * ref, (ref, fresh)
