@@ -20,9 +20,14 @@
 //     MFMAs add hi*hi + hi*lo + lo*hi (the lo*lo term is below fp32 rounding).
 //   * Angles: the keys of a block have consecutive n = j - f(j) (steps of 0 or 1), so
 //     R(n) = R(n0) R(n - n0) with n - n0 < 16.  Each lane of a wave owns one RoPE pair
-//     and evaluates cos/sin(n0 theta_m) in fp64 once per block (rounded once to fp32,
-//     the values a precomputed table would hold); the 16 offset rows R(d) are built
-//     once per workgroup.  No table is read, so decode needs no table in the workspace.
+//     and holds cos/sin(n0 theta_m) of the wave's current block in fp64, rounded to fp32
+//     per block (the values a precomputed table would hold); the 16 offset rows R(d) are
+//     built once per workgroup.  Consecutive blocks of a wave lie nsplit*16 keys apart,
+//     so n0 advances by one of two integers (the floor map moves by q or q + 1, with
+//     q = floor(nsplit*16 / G)): the fp64 angle pair advances by the angle-addition
+//     formula with one of two step rotations evaluated once per wave, and the drift
+//     after thousands of steps stays near 1e-12, far below fp32 rounding.  No table is
+//     read, so decode needs no table in the workspace.
 //   * O^T = V^T P^T (v_mfma_f32_16x16x16_bf16): the block's V rows are transposed
 //     through a per-wave LDS tile (pairs of keys packed per 32-bit word), P goes
 //     through a small LDS row buffer.
@@ -110,6 +115,9 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   __shared__ __align__(16) float2 s_row[NWD][64];
   // offset rows R(d), d = 0..15, padded by 16 B
   __shared__ __align__(16) float2 s_dt[BK][64 + 2];
+  // K tile of the current block per wave: 16 rows x 256 bytes (after the key loop, the
+  // wave's part of the merge buffer)
+  __shared__ __align__(16) uint8_t s_kt[NWD][BK * D * 2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -146,32 +154,71 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   const uint32_t rs = (uint32_t)a.Hkv * D;  // elements between consecutive cache rows
   const uint16_t* kg = (const uint16_t*)a.K + (size_t)b * a.seq_stride + (size_t)g * D;
   const uint16_t* vg = (const uint16_t*)a.V + (size_t)b * a.seq_stride + (size_t)g * D;
-  // Block loads, one block ahead: K (key l16, channels 32s + 8kq + e) and V (keys 2kp,
-  // 2kp+1 of channel group cg = 16 channels).  Keys past pos are clamped to pos (their
+  // Block loads, one block ahead, to registers.  K: load t takes keys 4t .. 4t+3 of the
+  // block, each a whole 256-byte row (lane: key 4t + (lane >> 4), 16-byte chunk
+  // lane & 15), so one load reads four contiguous row segments; loads that give each key
+  // 64 bytes stream about a tenth slower.  The chunks then go through the wave's LDS tile
+  // to the matrix-core layout (chunk c of key r at position c ^ r of its LDS row, which
+  // keeps both the writes and the reads free of bank conflicts).  V: lane (kp, cg) takes
+  // keys 2kp, 2kp+1, channels 8cg .. 8cg+7 and 64 + 8cg .. 64 + 8cg+7, so the eight lanes
+  // of a key cover 128 contiguous bytes per load.  Keys past pos are clamped to pos (their
   // scores are masked).
   const int kp = lane & 7, cg = lane >> 3;
   struct Blk {
-    uint4 k[4];
+    u32x4 k[4];  // native vectors: plain register moves, no struct copies
     uint4 v[2][2];
   };
+  // Byte offsets of this lane's loads within a block of 16 whole keys (key rows rs
+  // elements apart), fixed for the wave
+  uint32_t koff[4], voff[2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) koff[t] = ((4 * t + (lane >> 4)) * rs + 8 * (lane & 15)) * 2u;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) voff[k2] = ((2 * kp + k2) * rs + 8 * cg) * 2u;
   auto load_blk = [&](int i, Blk& x) __attribute__((always_inline)) {
     const int j0 = jb + (w + i * nsplit) * BK;
     // 64-bit offset of the block (uniform), 32-bit offsets of the lanes within it.  A
     // wave without blocks still loads one (the static wait counts): its j0 lies past
     // pos, so the base is clamped to pos too and every lane offset stays in [0, 15].
     const int jbase = min(j0, pos);
-    const uint16_t* kb = kg + (size_t)jbase * rs;
-    const uint16_t* vb = vg + (size_t)jbase * rs;
-    const int jk = min(j0 + l16, pos);
-    const uint16_t* kr = kb + (uint32_t)(jk - jbase) * rs + 8 * kq;
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(kg + (size_t)jbase * rs);
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(vg + (size_t)jbase * rs);
+    uint32_t ko[4], vo[2];
+    if (j0 + BK - 1 <= pos) {  // every key of the block exists (all but the last block)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kr + 32 * s);
+      for (int t = 0; t < 4; ++t) ko[t] = koff[t];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int jv = min(j0 + 2 * kp + k2, pos);
-      const uint16_t* vr = vb + (uint32_t)(jv - jbase) * rs + 16 * cg;
+      for (int k2 = 0; k2 < 2; ++k2) vo[k2] = voff[k2];
+    } else {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) x.v[k2][c] = *reinterpret_cast<const uint4*>(vr + 8 * c);
+      for (int t = 0; t < 4; ++t)
+        ko[t] = ((uint32_t)(min(j0 + 4 * t + (lane >> 4), pos) - jbase) * rs + 8 * (lane & 15)) * 2u;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        vo[k2] = ((uint32_t)(min(j0 + 2 * kp + k2, pos) - jbase) * rs + 8 * cg) * 2u;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x.k[t] = *reinterpret_cast<const u32x4*>(kb + ko[t]);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        x.v[k2][c] = *reinterpret_cast<const uint4*>(vb + vo[k2] + 128 * c);
+  };
+  // K of a block through the wave's LDS tile: lane (key l16, group kq), step s =
+  // channels 32s + 8kq .. +7 (chunk 4s + kq).  The wave's LDS operations run in order, so
+  // the reads see this block's writes and the next block's writes follow these reads.
+  uint8_t* kt = s_kt[wave];
+  auto stage_k = [&](const Blk& x, uint4* k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 4 * t + (lane >> 4);
+      *reinterpret_cast<u32x4*>(kt + 256 * r + 16 * ((lane & 15) ^ r)) = x.k[t];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 y = *reinterpret_cast<const u32x4*>(kt + 256 * l16 + 16 * ((4 * s + kq) ^ l16));
+      k[s] = make_uint4(y[0], y[1], y[2], y[3]);
     }
   };
 
@@ -195,6 +242,18 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     s_dt[r][lane] = angle_cs(variant == kVariantInterp ? r * rpos : (double)r, invf);
   row[lane] = angle_cs(variant == kVariantInterp ? pos * rpos : (double)(pos - alias_fast(pos, gdiv)),
                        invf);
+  // fp64 angle of the current block (first block: w) and the two step rotations
+  const int jstep = nsplit * BK;
+  const int dstep = jstep - alias_fast(jstep, gdiv);  // n0 step when f moves by floor(jstep/G)
+  double ac, as, ca, sa, cb, sb;
+  {
+    const int jw = jb + w * BK;
+    const double a0 = variant == kVariantInterp ? jw * rpos : (double)(jw - alias_fast(jw, gdiv));
+    sincos_reduced(a0 * invf, &as, &ac);
+    const double da = variant == kVariantInterp ? jstep * rpos : (double)dstep;
+    sincos_reduced(da * invf, &sa, &ca);
+    sincos_reduced((da - 1.0) * invf, &sb, &cb);
+  }
 
   // ---- query operands (A: rows = query heads, lanes l16 >= REP zero) ------------------
   // lane (head l16, group kq) holds channels 32s + 8kq + e, s = 0..3
@@ -244,17 +303,21 @@ decode_mfma_kernel(DecodeBatchArgs a) {
 
   uint16_t* vt = s_vt[wave];
   uint16_t* pt = s_p[wave];
-  // Blocks alternate between two load buffers (no register copy between blocks).
+  // Blocks alternate between two load buffers (no register copy between blocks): block
+  // i + 1's loads go out first and stay in flight while block i is scored.
   auto block = [&](int i, const Blk& cur, Blk& nxt) __attribute__((always_inline)) {
     const int j0 = jb + (w + i * nsplit) * BK;  // <= pos
     const int jk = j0 + l16;
     const bool any_remote = j0 <= last_remote;
+    const int n0 = j0 - alias_fast(j0, gdiv);  // n of the block's first key (floor map)
     const bool any_local = j0 + BK - 1 > last_remote;
     // unconditional (the last block reloads itself): a static count of loads in
     // flight keeps the waits below from draining the prefetch
     load_blk(min(i + 1, cnt - 1), nxt);
+    uint4 kr4[4];
+    stage_k(cur, kr4);
 
-    // ---- V^T tile: keys (2kp, 2kp+1) of channels 16cg .. 16cg+15, one word each --------
+    // ---- V^T tile: keys (2kp, 2kp+1) of channels 64c + 8cg + e, one word each ----------
     // row dd: four 8-byte segments of 4 keys; segment q sits at q ^ ((dd >> 2) & 3)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -264,7 +327,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
       for (int ww = 0; ww < 4; ++ww) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int dd = 16 * cg + 8 * c + 2 * ww + hh;
+          const int dd = 64 * c + 8 * cg + 2 * ww + hh;
           const uint32_t word = __byte_perm(a0[ww], a1[ww], hh ? 0x7632 : 0x5410);
           const int seg = (kp >> 1) ^ ((dd >> 2) & 3);
           *reinterpret_cast<uint32_t*>(vt + dd * BK + 4 * seg + 2 * (kp & 1)) = word;
@@ -276,13 +339,12 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
     if (any_remote) {
       const int jkc = min(jk, pos);
-      // n of the block's first key and the offset row of this lane's key: floor map
-      // (n steps by 0 or 1 per key) or continuous map (n = j rpos, offset row j - j0)
-      const int n0 = j0 - alias_fast(j0, gdiv);
+      // offset row of this lane's key: floor map (n steps by 0 or 1 per key) or
+      // continuous map (n = j rpos, offset row j - j0)
       const int dk = variant == kVariantInterp ? jkc - j0 : (jkc - alias_fast(jkc, gdiv)) - n0;
       // R(n0) of the block: lane = pair (the wave's previous reads of the row are
       // complete: LDS operations of a wave execute in order)
-      row[lane] = angle_cs(variant == kVariantInterp ? j0 * rpos : (double)n0, invf);
+      row[lane] = make_float2((float)ac, (float)as);
       const float2* drow = &s_dt[dk][8 * kq];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -294,9 +356,9 @@ decode_mfma_kernel(DecodeBatchArgs a) {
           const float4 cd = *reinterpret_cast<const float4*>(drow + 32 * s + 2 * e2);
           const float4 cs = make_float4(c0.x * cd.x - c0.y * cd.y, c0.y * cd.x + c0.x * cd.y,
                                         c0.z * cd.z - c0.w * cd.w, c0.w * cd.z + c0.z * cd.w);
-          rot_neg(bf16_at(cur.k[s], 2 * e2), bf16_at(cur.k[s + 2], 2 * e2), cs.x, cs.y,
+          rot_neg(bf16_at(kr4[s], 2 * e2), bf16_at(kr4[s + 2], 2 * e2), cs.x, cs.y,
                   y1[2 * e2], y2[2 * e2]);
-          rot_neg(bf16_at(cur.k[s], 2 * e2 + 1), bf16_at(cur.k[s + 2], 2 * e2 + 1), cs.z, cs.w,
+          rot_neg(bf16_at(kr4[s], 2 * e2 + 1), bf16_at(kr4[s + 2], 2 * e2 + 1), cs.z, cs.w,
                   y1[2 * e2 + 1], y2[2 * e2 + 1]);
         }
         u32x4 h1, l1, h2, l2;
@@ -314,7 +376,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const u32x4 qs = *reinterpret_cast<const u32x4*>(sq_row + 32 * s);
-        sl = mfma16_bf16(qs, __builtin_bit_cast(u32x4, cur.k[s]), sl);
+        sl = mfma16_bf16(qs, __builtin_bit_cast(u32x4, kr4[s]), sl);
       }
     }
     const bool use_local = pos - jk < a.w0;
@@ -370,6 +432,16 @@ decode_mfma_kernel(DecodeBatchArgs a) {
       const uint2 va = *reinterpret_cast<const uint2*>(vt + d * BK + 4 * seg);
       oacc[db] = mfma16k16_bf16(va, pb, oacc[db]);
     }
+
+    // ---- advance the block angle to this wave's next block --------------------------------
+    const int j1 = j0 + jstep;
+    if (j1 <= last_remote) {
+      const bool alt = variant != kVariantInterp && (j1 - alias_fast(j1, gdiv)) - n0 != dstep;
+      const double c = alt ? cb : ca, sn = alt ? sb : sa;
+      const double t = ac * c - as * sn;
+      as = fma(as, c, ac * sn);
+      ac = t;
+    }
   };
   int i = 0;
   for (; i + 1 < cnt; i += 2) {
@@ -383,7 +455,10 @@ decode_mfma_kernel(DecodeBatchArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) lt[r] = row_sum(l_run[r]);
   __shared__ float s_ml[NWD][16][2];
-  __shared__ __align__(16) float s_acc[NWD][8][D];  // [wave][head][channel]
+  // [wave][head][channel] over the K tiles: each wave writes the part that was its own
+  // tile, after its own last reads of it
+  float(*s_acc)[8][D] = reinterpret_cast<float(*)[8][D]>(&s_kt[0][0]);
+  static_assert(sizeof(s_kt[0]) == sizeof(float) * 8 * D, "merge buffer = K tile per wave");
   if (l16 == 0)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

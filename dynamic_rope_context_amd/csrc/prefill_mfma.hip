@@ -421,19 +421,6 @@ __device__ __forceinline__ void wait_vm_barrier_w(int wave) {
   asm volatile("" ::: "memory");
 }
 
-// One 16-byte LDS-DMA transfer per lane: lane l's 16 bytes land at dst + 16 l.
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0,
-                                   0);
-}
-// The same from a wave-uniform base plus a 32-bit lane offset.  The empty asm keeps the
-// offset's zero extension next to the add, so the transfer takes the scalar-base form
-// instead of a 64-bit vector address computed per transfer.
-__device__ __forceinline__ void dma16_at(const uint8_t* base, uint32_t off, void* lds_dst) {
-  asm volatile("" : "+v"(off));
-  dma16(base + off, lds_dst);
-}
-
 template <int REP>
 __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   using namespace mf;
