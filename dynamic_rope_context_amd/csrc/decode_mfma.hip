@@ -55,20 +55,20 @@ constexpr float kLazy = 8.f;     // allowed growth of the running max before a r
 }  // namespace dm
 
 // fp16 hi/lo of 8 consecutive values, packed as two MFMA operands: hi = RNE(y) by the
-// packed conversion, lo = RNE(y - hi) with hi read back from the packed word (the asm
-// keeps the compiler from re-deriving hi with separate scalar conversions).
+// packed conversion, lo = RNE(y - hi).  y - hi is exact in fp32 (hi is y rounded to 11
+// bits, or inf on overflow, when the difference is -inf as well), so one mixed-precision
+// FMA per half, fp16 hi times -1 plus fp32 y rounded once to fp16, gives the same bits
+// as converting hi back and subtracting, in one instruction instead of three.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split8(const float* y, u32x4& hi, u32x4& lo) {
   uint32_t h[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const f16x2_t hv = {(_Float16)y[2 * e], (_Float16)y[2 * e + 1]};
-    uint32_t hb = __builtin_bit_cast(uint32_t, hv);
-    asm volatile("" : "+v"(hb));
-    const f16x2_t hr = __builtin_bit_cast(f16x2_t, hb);
-    const f16x2_t lv = {(_Float16)(y[2 * e] - (float)hr.x), (_Float16)(y[2 * e + 1] - (float)hr.y)};
-    h[e] = hb;
-    l[e] = __builtin_bit_cast(uint32_t, lv);
+    h[e] = __builtin_bit_cast(uint32_t, hv);
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l[e]) : "v"(h[e]), "v"(y[2 * e]));
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "+v"(l[e]) : "v"(h[e]), "v"(y[2 * e + 1]));
   }
   hi = u32x4{h[0], h[1], h[2], h[3]};
   lo = u32x4{l[0], l[1], l[2], l[3]};
