@@ -14,6 +14,11 @@ Prints one JSON line on stdout; progress goes to stderr.
   decode     KV GB/s = bytes of K and V read per step / step time, against 8000 GB/s
   decode_batch  a batch of 8 sequences of 16K rows each in one bifocal_decode_batch call
              per step (the same K + V bytes per step as the 128K sequence)
+  other_prefills  the Qwen3-1.7B-shaped 32K layer with G = 1 and the Qwen3-8B-shaped
+             ragged batch (98427 + 40001 tokens, G = 4 and 2 per sequence): ms per call,
+             TFLOP/s counted the same way and the fraction of the bf16 peak
+  rope_apply the standard-RoPE rotation of the 128K query tensor in place: us per call,
+             GB/s (every element read and written once) and the fraction of 8000 GB/s
   three_pass the literal inclusion-exclusion form of the same prefill (local/window,
              remote/causal and remote/window passes merged by their LSEs): time and the
              ratio to the fused call
