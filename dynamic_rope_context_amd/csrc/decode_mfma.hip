@@ -11,10 +11,13 @@
 // bytes as they are.
 //
 // Layout (per wave, 16 keys per block, 16x16 matrix-core shapes):
-//   * S = Q K^T with the query heads as MFMA rows and the block's keys as columns
-//     (v_mfma_f32_16x16x32): lane (key l, group k) of the B operand holds channels
+//   * S^T = K Q^T with the block's keys as MFMA rows and the query heads as columns
+//     (v_mfma_f32_16x16x32): lane (key l, group k) of the A operand holds channels
 //     32s + 8k + e of its key, so a channel and its RoPE partner (c + 64) sit in the
-//     same lane, steps s and s + 2.
+//     same lane, steps s and s + 2.  The result gives lane (head h, group k) keys
+//     4k .. 4k+3 of head h: the layout of P^T as the B operand of the PV product, so
+//     the probabilities never leave the registers, and a head's row max and sum take
+//     two lane swaps.
 //   * Remote scores need fp32 accuracy (the fp32 rotation is not representable in one
 //     16-bit operand): keys and query are split into fp16 hi + lo parts and three
 //     MFMAs add hi*hi + hi*lo + lo*hi (the lo*lo term is below fp32 rounding).
@@ -29,8 +32,7 @@
 //     after thousands of steps stays near 1e-12, far below fp32 rounding.  No table is
 //     read, so decode needs no table in the workspace.
 //   * O^T = V^T P^T (v_mfma_f32_16x16x16_bf16): the block's V rows are transposed
-//     through a per-wave LDS tile (pairs of keys packed per 32-bit word), P goes
-//     through a small LDS row buffer.
+//     through a per-wave LDS tile (pairs of keys packed per 32-bit word).
 //   * Online softmax in the base-2 domain with a lazy running max per head.
 //   * Two waves per SIMD (at most 256 registers each) so that one wave's loads are in
 //     flight while the other computes.
@@ -88,20 +90,23 @@ __device__ __forceinline__ f32x4 mfma16k16_bf16(uint2 a, uint2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
                                                    __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
 }
-// Max / sum over the 16 lanes of a DPP row.
-__device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));
-  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));
+// Max / sum of lane i and lane i ^ 16 (rows of 16 lanes swapped in pairs), and sums
+// of lane i and lane i ^ 32, with the permlane swaps (no LDS round trip).
+__device__ __forceinline__ float max_lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float row_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));
-  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));
+__device__ __forceinline__ float sum_lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
+__device__ __forceinline__ float sum_lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 template <int REP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeBatchArgs a) {
@@ -110,7 +115,6 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   // rows [16 heads][16 keys], standard query rows [8 heads][128] + one zero row, and
   // the angle row R(n0) of the current block (lane = RoPE pair)
   __shared__ __align__(16) uint16_t s_vt[NWD][D * BK];
-  __shared__ __align__(16) uint16_t s_p[NWD][16 * BK];
   __shared__ __align__(16) uint16_t s_q[NWD][9 * D];
   __shared__ __align__(16) float2 s_row[NWD][64];
   // offset rows R(d), d = 0..15, padded by 16 B
@@ -294,15 +298,11 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   f32x4 oacc[8];  // O^T blocks [16 channels][16 head columns]
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];  // heads 4*kq + r, base-2 domain; l per lane (summed at the end)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -1e30f;
-    l_run[r] = 0.f;
-  }
+  // running max of head l16 (base-2 domain, equal in the lane's four key groups) and
+  // the lane's share of its row sum (keys 4kq .. 4kq+3 of every block; summed at the end)
+  float m_run = -1e30f, l_run = 0.f;
 
   uint16_t* vt = s_vt[wave];
-  uint16_t* pt = s_p[wave];
   // Blocks alternate between two load buffers (no register copy between blocks): block
   // i + 1's loads go out first and stay in flight while block i is scored.
   auto block = [&](int i, const Blk& cur, Blk& nxt) __attribute__((always_inline)) {
@@ -364,67 +364,55 @@ decode_mfma_kernel(DecodeBatchArgs a) {
         u32x4 h1, l1, h2, l2;
         split8(y1, h1, l1);
         split8(y2, h2, l2);
-        sr = mfma16_f16(qh[s], h1, sr);
-        sr = mfma16_f16(qh[s], l1, sr);
-        sr = mfma16_f16(ql[s], h1, sr);
-        sr = mfma16_f16(qh[s + 2], h2, sr);
-        sr = mfma16_f16(qh[s + 2], l2, sr);
-        sr = mfma16_f16(ql[s + 2], h2, sr);
+        sr = mfma16_f16(h1, qh[s], sr);
+        sr = mfma16_f16(l1, qh[s], sr);
+        sr = mfma16_f16(h1, ql[s], sr);
+        sr = mfma16_f16(h2, qh[s + 2], sr);
+        sr = mfma16_f16(l2, qh[s + 2], sr);
+        sr = mfma16_f16(h2, ql[s + 2], sr);
       }
     }
     if (any_local) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const u32x4 qs = *reinterpret_cast<const u32x4*>(sq_row + 32 * s);
-        sl = mfma16_bf16(qs, __builtin_bit_cast(u32x4, kr4[s]), sl);
+        sl = mfma16_bf16(__builtin_bit_cast(u32x4, kr4[s]), qs, sl);
       }
     }
-    const bool use_local = pos - jk < a.w0;
-    // window-only variant: keys before the window are dropped, not re-scored
-    const bool valid = jk <= pos && (variant != kVariantWindow || use_local);
+    // S^T: lane (head l16, group kq) holds keys j0 + 4kq + r, r = 0..3, of head l16
     float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = valid ? (use_local ? sl[r] : sr[r]) : -INFINITY;
-
-    // ---- online softmax (heads 4kq + r: row group kq of the result) ---------------------
-    float bm[4];
-    bool need = false;
-#pragma unroll
     for (int r = 0; r < 4; ++r) {
-      bm[r] = fmaxf(m_run[r], row_max(sc[r]) * c2);
-      need |= bm[r] > m_run[r] + kLazy;
+      const int j = j0 + 4 * kq + r;
+      const bool use_local = pos - j < a.w0;
+      // window-only variant: keys before the window are dropped, not re-scored
+      const bool valid = j <= pos && (variant != kVariantWindow || use_local);
+      sc[r] = valid ? (use_local ? sl[r] : sr[r]) : -INFINITY;
     }
+
+    // ---- online softmax of head l16 -------------------------------------------------------
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = max_lane_xor16(max_lane_xor32(mx));  // the head's four key groups
+    const float bm = fmaxf(m_run, mx * c2);
+    const bool need = bm > m_run + kLazy;
     if (__ballot(need)) {
-      float f[4];
+      // O^T column l16 is head l16: the lane's own factor
+      const float mn = need ? bm : m_run;
+      const float f = fast_exp2(m_run - mn);
+      l_run *= f;
+      m_run = mn;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float mn = bm[r] > m_run[r] + kLazy ? bm[r] : m_run[r];
-        f[r] = fast_exp2(m_run[r] - mn);
-        l_run[r] *= f[r];
-        m_run[r] = mn;
-      }
-      // O^T column l16 belongs to head l16: its factor lives in row group l16 >> 2,
-      // register l16 & 3
-      const int src = 16 * ((l16 >> 2) & 3);
-      float fc = 1.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float fr = __shfl(f[r], src);
-        if ((l16 & 3) == r) fc = fr;
-      }
-#pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[db] *= fc;
+      for (int db = 0; db < 8; ++db) oacc[db] *= f;
     }
+    float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(__fmaf_rn(sc[r], c2, -m_run[r]));
-      l_run[r] += p;
-      const int h = 4 * kq + r;
-      if (h < REP) pt[h * BK + l16] = (uint16_t)(pack_bf16(p, 0.f) & 0xffffu);
+      pr[r] = fast_exp2(__fmaf_rn(sc[r], c2, -m_run));
+      l_run += pr[r];
     }
 
-    // ---- O^T += V^T P^T (K = the block's 16 keys) -----------------------------------------
-    const uint2 pb = *reinterpret_cast<const uint2*>(pt + (l16 & 15) * BK + 4 * kq);
+    // ---- O^T += V^T P^T (K = the block's 16 keys): P^T is already in operand layout ------
+    const uint2 pb = make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const int d = 16 * db + l16;
@@ -451,20 +439,16 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   if (i < cnt) block(i, buf0, buf1);
 
   // ---- merge the four waves (splits) of this workgroup, write one partial per head -----
-  float lt[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) lt[r] = row_sum(l_run[r]);
+  const float lt = sum_lane_xor16(sum_lane_xor32(l_run));  // the head's four key groups
   __shared__ float s_ml[NWD][16][2];
   // [wave][head][channel] over the K tiles: each wave writes the part that was its own
   // tile, after its own last reads of it
   float(*s_acc)[8][D] = reinterpret_cast<float(*)[8][D]>(&s_kt[0][0]);
   static_assert(sizeof(s_kt[0]) == sizeof(float) * 8 * D, "merge buffer = K tile per wave");
-  if (l16 == 0)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s_ml[wave][4 * kq + r][0] = cnt > 0 ? m_run[r] : -INFINITY;
-      s_ml[wave][4 * kq + r][1] = cnt > 0 ? lt[r] : 0.f;
-    }
+  if (kq == 0) {
+    s_ml[wave][l16][0] = cnt > 0 ? m_run : -INFINITY;
+    s_ml[wave][l16][1] = cnt > 0 ? lt : 0.f;
+  }
   if (l16 < REP) {  // O^T column l16 = head l16: rows 16db + 4kq + r
 #pragma unroll
     for (int db = 0; db < 8; ++db)

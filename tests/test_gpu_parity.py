@@ -103,6 +103,33 @@ def test_rope_apply_matches_oracle(bf, dt, G, use_pos, D):
         assert np.max(np.abs(got - exact)) <= 4e-7 * mag
 
 
+@pytest.mark.parametrize("dt,T,H,D", [("bf16", 61, 40, 128), ("f32", 61, 40, 128),
+                                      ("bf16", 17, 64, 64), ("f32", 9, 33, 128),
+                                      ("bf16", 1, 262145, 128)])
+def test_rope_apply_many_heads(bf, dt, T, H, D):
+    # several rounds of loads per workgroup (8 tokens x H x D/16 chunks beyond 8 (bf16)
+    # or 4 (fp32) per thread), ragged token blocks, and H * D past 2^25, which takes the
+    # one-pair-per-thread kernel
+    say(f"rope_apply many heads dt={dt} T={T} H={H} D={D}")
+    rng = np.random.default_rng(11)
+    theta, G = 1e6, 3
+    x = to_dtype(rng.standard_normal((T, H, D)).astype(np.float32), dt)
+    pos = rng.integers(0, 131072, size=T).astype(np.int32)
+    xd = dev(x, dt)
+    bf.rope_apply(xd, theta, pos=torch.from_numpy(pos).cuda(), G=G)
+    torch.cuda.synchronize()
+    got = host(xd).astype(np.float64)
+    exact = rope_apply_ref(x, pos, theta, G)
+    x64 = x.astype(np.float64)
+    mag = np.abs(x64[..., :D // 2]) + np.abs(x64[..., D // 2:])
+    mag = np.concatenate([mag, mag], axis=-1)
+    if dt == "bf16":
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
+        assert np.all(np.abs(got - exact) <= ulp + 4 * 2.0 ** -24 * mag)
+    else:
+        assert np.max(np.abs(got - exact)) <= 4e-7 * mag.max()
+
+
 # ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
