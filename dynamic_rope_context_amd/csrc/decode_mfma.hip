@@ -24,8 +24,8 @@
 //   * Angles: the keys of a block have consecutive n = j - f(j) (steps of 0 or 1), so
 //     R(n) = R(n0) R(n - n0) with n - n0 < 16.  Each lane of a wave owns one RoPE pair
 //     and holds cos/sin(n0 theta_m) of the wave's current block in fp64, rounded to fp32
-//     per block (the values a precomputed table would hold); the 16 offset rows R(d) are
-//     built once per workgroup.  Consecutive blocks of a wave lie nsplit*16 keys apart,
+//     per block (the values a precomputed table would hold, to within fp32 rounding);
+//     the 16 offset rows R(d) are built once per workgroup.  Consecutive blocks of a wave lie nsplit*16 keys apart,
 //     so n0 advances by one of two integers (the floor map moves by q or q + 1, with
 //     q = floor(nsplit*16 / G)): the fp64 angle pair advances by the angle-addition
 //     formula with one of two step rotations evaluated once per wave, and the drift
@@ -119,6 +119,10 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   __shared__ __align__(16) float2 s_row[NWD][64];
   // offset rows R(d), d = 0..15, padded by 16 B
   __shared__ __align__(16) float2 s_dt[BK][64 + 2];
+  // angles computed once per workgroup: the offset rows' base step and the block
+  // recurrence's step (fp64), the query's row (fp32)
+  __shared__ __align__(16) double2 s_base[64], s_step[64];
+  __shared__ __align__(16) float2 s_qrow[64];
   // K tile of the current block per wave: 16 rows x 256 bytes (after the key loop, the
   // wave's part of the merge buffer)
   __shared__ __align__(16) uint8_t s_kt[NWD][BK * D * 2];
@@ -240,23 +244,53 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   const double invf = inv_freq64(a.theta, lane, D);  // lane = RoPE pair
   float2* row = s_row[wave];
 
-  // ---- angles: offset rows (shared) and the query's row --------------------------------
-#pragma unroll
-  for (int r = wave; r < BK; r += NWD)
-    s_dt[r][lane] = angle_cs(variant == kVariantInterp ? r * rpos : (double)r, invf);
-  row[lane] = angle_cs(variant == kVariantInterp ? pos * rpos : (double)(pos - alias_fast(pos, gdiv)),
-                       invf);
-  // fp64 angle of the current block (first block: w) and the two step rotations
+  // ---- angles ----------------------------------------------------------------------------
+  // Each wave takes one float64 sincos per lane for its first block; three angles are
+  // shared by the workgroup, one wave each: the offset rows' base step (wave 0), the
+  // query's row (wave 1) and the block recurrence's step (wave 2).  The offset rows are
+  // float64 powers of the base step and R(step - 1) = R(step) R(-1), so a wave evaluates
+  // two sincos instead of eight (products of a few unit rotations stay within 1e-15 of
+  // the sincos values, far below fp32 rounding).
   const int jstep = nsplit * BK;
   const int dstep = jstep - alias_fast(jstep, gdiv);  // n0 step when f moves by floor(jstep/G)
-  double ac, as, ca, sa, cb, sb;
+  const double da = variant == kVariantInterp ? jstep * rpos : (double)dstep;
+  double ac, as;  // fp64 angle of the current block (first block: w)
   {
     const int jw = jb + w * BK;
     const double a0 = variant == kVariantInterp ? jw * rpos : (double)(jw - alias_fast(jw, gdiv));
     sincos_reduced(a0 * invf, &as, &ac);
-    const double da = variant == kVariantInterp ? jstep * rpos : (double)dstep;
-    sincos_reduced(da * invf, &sa, &ca);
-    sincos_reduced((da - 1.0) * invf, &sb, &cb);
+  }
+  if (wave == 0) {
+    double sn, cs;  // base step: 1 (floor map) or G-1/G (continuous map)
+    sincos_reduced((variant == kVariantInterp ? rpos : 1.0) * invf, &sn, &cs);
+    s_base[lane] = make_double2(cs, sn);
+  } else if (wave == 1) {
+    s_qrow[lane] = angle_cs(variant == kVariantInterp ? pos * rpos
+                                                     : (double)(pos - alias_fast(pos, gdiv)),
+                            invf);
+  } else if (wave == 2) {
+    double sn, cs;
+    sincos_reduced(da * invf, &sn, &cs);
+    s_step[lane] = make_double2(cs, sn);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // shared angles written
+  auto cmul = [](double2 x, double2 y) __attribute__((always_inline)) {
+    return make_double2(x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x);
+  };
+  const double2 b1 = s_base[lane];
+  const double2 st = s_step[lane];
+  const double ca = st.x, sa = st.y;
+  // R(da - 1) = R(da) conj(R(1)) (floor map; the continuous map never takes it)
+  const double cb = ca * b1.x + sa * b1.y, sb = sa * b1.x - ca * b1.y;
+  {
+    // offset rows d = wave + 4k: B^d with B the base step
+    const double2 p2 = cmul(b1, b1), p4 = cmul(p2, p2);
+    double2 r = wave == 0 ? make_double2(1.0, 0.0) : wave == 1 ? b1 : wave == 2 ? p2 : cmul(p2, b1);
+#pragma unroll
+    for (int k = 0; k < BK / NWD; ++k) {
+      s_dt[wave + NWD * k][lane] = make_float2((float)r.x, (float)r.y);
+      r = cmul(r, p4);
+    }
   }
 
   // ---- query operands (A: rows = query heads, lanes l16 >= REP zero) ------------------
@@ -277,7 +311,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float y1[8], y2[8];
-      const float4* tr = reinterpret_cast<const float4*>(row + 32 * s + 8 * kq);
+      const float4* tr = reinterpret_cast<const float4*>(s_qrow + 32 * s + 8 * kq);
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const float4 cs = tr[e2];
