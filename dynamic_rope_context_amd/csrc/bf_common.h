@@ -52,16 +52,8 @@ constexpr int kSelPairs = 4;  // RoPE pairs per KV head given the hi/lo correcti
 // the power-of-two exponents e that keep the fp16 operands in range (remote queries of
 // the group, remote keys, values: each operand is multiplied by 2^-e before its fp16
 // rounding, and the product is scaled back exactly).
-// Then, for the query-side correction of each query head of the group: a channel order
-// (kSelPerm: 128 channel indices, one byte each, position p holds channel perm[p]) in
-// which slice r (positions 16r .. 16r+15) holds the up to kHeadPairs pairs chosen for query
-// head r (pair j at 16r + j and its partner channel at 16r + 8 + j), and per head the
-// mask of slice positions that carry a chosen pair (kSelMask + r, 16 bits).
-constexpr int kHeadPairs = 8;
 constexpr int kSelExpQ = kSelPairs, kSelExpK = kSelPairs + 1, kSelExpV = kSelPairs + 2;
-constexpr int kSelPerm = 8;               // 32 words = 128 bytes
-constexpr int kSelMask = kSelPerm + 32;   // 8 words (query heads of a group, up to 8)
-constexpr int kSelStride = kSelMask + 8;
+constexpr int kSelStride = 8;
 constexpr size_t kKeyTileBytes = 17408;  // one prefill key-tile record (32 keys, D = 128)
 constexpr int kKeyTileKeys = 32;
 

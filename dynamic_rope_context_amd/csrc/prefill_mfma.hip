@@ -142,20 +142,12 @@ __device__ __forceinline__ void wave_argmax(float v, int& bi, float& bv) {
 //    tokens) get the hi/lo correction on both sides for every query head of the group
 //    (the key-tile records carry their key remainders): the sum ranks first the pairs
 //    that are large in the key, whose rounding errors reach every head;
-//  * then each query head r of the group in turn takes up to kHeadPairs of the remaining
-//    pairs with the largest |q_r,m|^2 * |k_m|^2 for a query-side correction (its query
-//    remainder against the fp16 key), laid out as slice r of a channel order that the
-//    remote key copies and query operands share (the other channels fill the free
-//    positions in increasing order);
 //  * the operand exponents of the group's remote queries, remote keys and values.
 __global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restrict__ mxq,
                                                          const uint32_t* __restrict__ mxk,
                                                          const uint32_t* __restrict__ mxv,
                                                          int Hq, int Hkv,
                                                          int32_t* __restrict__ sel) {
-  __shared__ int s_slot[64];  // pair -> query head * kHeadPairs + slot, or -1
-  __shared__ uint8_t s_perm[128];
-  __shared__ bool s_used[128];
   const int g = blockIdx.x, m = threadIdx.x;
   const int rep = Hq / Hkv;
   int32_t* rec = sel + g * kSelStride;
@@ -176,21 +168,6 @@ __global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restr
     if (m == 0) rec[p] = bi;
     if (m == bi) taken = true;
   }
-  int slot = -1;
-  for (int r = 0; r < rep; ++r) {
-    const float b = __uint_as_float(mxq[(g * rep + r) * 64 + m]) * kk;
-    for (int j = 0; j < kHeadPairs; ++j) {
-      int bi;
-      float bv;
-      wave_argmax(taken ? -1.f : b, bi, bv);
-      if (bv < 0.f) break;  // every pair taken (wave-uniform)
-      if (m == bi) {
-        taken = true;
-        slot = r * kHeadPairs + j;
-      }
-    }
-  }
-  s_slot[m] = slot;
   float qm = q, km = kk;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -198,45 +175,17 @@ __global__ void __launch_bounds__(64) pair_select_kernel(const uint32_t* __restr
     km = fmaxf(km, __shfl_xor(km, o));
     vv = fmaxf(vv, __shfl_xor(vv, o));
   }
-  __syncthreads();
   if (m == 0) {
     rec[kSelExpQ] = fp16_range_exp(qm);
     rec[kSelExpK] = fp16_range_exp(km);
     rec[kSelExpV] = fp16_range_exp(vv);
-    uint8_t* perm = s_perm;
-    bool* used = s_used;
-    uint32_t mask[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i = 0; i < 128; ++i) used[i] = false;
-    for (int pm = 0; pm < 64; ++pm) {
-      const int sl = s_slot[pm];
-      if (sl < 0) continue;
-      const int r = sl / kHeadPairs, j = sl % kHeadPairs;
-      perm[16 * r + j] = (uint8_t)pm;
-      perm[16 * r + 8 + j] = (uint8_t)(pm + 64);
-      used[16 * r + j] = used[16 * r + 8 + j] = true;
-      mask[r] |= (1u << j) | (1u << (8 + j));
-    }
-    int free_pos = 0;
-    for (int c = 0; c < 128; ++c) {
-      if (s_slot[c & 63] >= 0) continue;  // placed in its head's slice
-      while (used[free_pos]) ++free_pos;
-      perm[free_pos] = (uint8_t)c;
-      used[free_pos] = true;
-    }
-    for (int w = 0; w < 32; ++w)
-      rec[kSelPerm + w] = (int32_t)((uint32_t)perm[4 * w] | ((uint32_t)perm[4 * w + 1] << 8) |
-                                    ((uint32_t)perm[4 * w + 2] << 16) |
-                                    ((uint32_t)perm[4 * w + 3] << 24));
-    for (int r = 0; r < 8; ++r) rec[kSelMask + r] = (int32_t)mask[r];
   }
 }
 
 // ---------------------------------------------------------------------------
 // Key preparation: once per call, each key tile of each KV head is turned into the
 // record the main kernel copies into LDS verbatim (layout in prefill_args.h): the
-// remote copy R(f(j) - j) K_j 2^-e_k rounded to fp16, its channels in the KV head's
-// order from the pre-pass (slice r holds query head r's corrected pairs), the hi/lo
-// correction of the
+// remote copy R(f(j) - j) K_j 2^-e_k rounded to fp16, the hi/lo correction of the
 // selected pairs, and V^T 2^-e_v in fp16 (the PV operands are fp16: P keeps 11
 // significant bits instead of 8).  A key is rotated once here instead of once per query block that
 // reads it.  One workgroup (256 threads) per (tile, KV head).
@@ -248,7 +197,6 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
   using namespace mf;
   __shared__ __align__(16) uint16_t sv[BK][D + 8];
   __shared__ __align__(16) float sy[BK][D + 4];  // rotated keys, natural channel order
-  __shared__ uint8_t s_perm[D];
   __shared__ double s_invf[D / 2];  // theta_m (continuous remote positions only)
   const int g = blockIdx.y;
   const int t_local = blockIdx.x;
@@ -341,19 +289,13 @@ __global__ void __launch_bounds__(256) key_prep_kernel(PrefillArgs args) {
         *reinterpret_cast<uint4*>(&sy[k][64 * q + 8 * p + 4]) = zero;
       }
     }
-    if (tid < 32) {  // the shared channel order of the remote operands, one byte each
-      const uint32_t w = (uint32_t)args.sel[g * kSelStride + kSelPerm + tid];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_perm[4 * tid + e] = (uint8_t)(w >> (8 * e));
-    }
     __syncthreads();
-    // record position q of key k holds channel perm[q]
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       uint32_t h[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        h[e] = pack_f16(sy[k][s_perm[64 * q + 8 * p + 2 * e]], sy[k][s_perm[64 * q + 8 * p + 2 * e + 1]]);
+        h[e] = pack_f16(sy[k][64 * q + 8 * p + 2 * e], sy[k][64 * q + 8 * p + 2 * e + 1]);
       *reinterpret_cast<uint4*>(kr + k * D + 64 * q + 8 * p) = make_uint4(h[0], h[1], h[2], h[3]);
     }
     if (tid < 4 * BK) {
@@ -502,24 +444,18 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   auto vt_kt = [&](int v) __attribute__((always_inline)) { return v < nr ? r0 + v : ktA + (v - nr); };
 
   // ---- query operands -------------------------------------------------------------
-  // B operand of S^T = K Q^T: lane (column ln, half hf) holds operand positions
-  // 16s + 8hf + e.  Local pass: the bf16 query, channel = position.  Remote pass: the fp16
-  // of R(f(i)-i) q 2^-e_q with the channels in the KV head's order from the pre-pass
-  // (position p holds channel perm[p], the order of the remote key copies), so that slice
-  // hr holds the pairs chosen for this wave's query head.
+  // B operand of S^T = K Q^T: lane (column ln, half hf) holds channels 16s + 8hf + e.
+  // Local pass: the bf16 query.  Remote pass: the fp16 of R(f(i)-i) q 2^-e_q.
   u32x4 qop[8];
   u32x4 qcor;     // hi (half 0) or lo (half 1) of the 8 channels of the both-sided pairs
-  u32x4 qcorh;    // fp16 remainders of slice hr (zero at positions without a chosen pair)
-  const int hr = wave / PBLK;  // this wave's query head within the group
   auto load_q_std = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
   };
   const float qs = __builtin_ldexpf(1.f, -args.sel[g * kSelStride + kSelExpQ]);
   // Runs before any transfer into the LDS ring, whose space holds the rotated rows of
-  // each wave meanwhile (natural channel order, float32) for the gather into the channel
-  // order; the workgroup meets twice.
-  __shared__ uint8_t s_qperm[D];
+  // each wave meanwhile (float32) for the gather of the corrected pairs' channels; the
+  // workgroup meets twice.
   auto load_q_remote = [&]() __attribute__((always_inline)) {
     constexpr int QS_LD = D + 4;  // floats per staged row
     float* stg = reinterpret_cast<float*>(smem_raw) + wave * (32 * QS_LD) + ln * QS_LD;
@@ -539,6 +475,11 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         y1[e] *= qs;
         y2[e] *= qs;
       }
+      // channels 16s + 8hf + e (s < 4) and their partners (operand s + 4)
+      qop[s] = u32x4{pack_f16(y1[0], y1[1]), pack_f16(y1[2], y1[3]), pack_f16(y1[4], y1[5]),
+                     pack_f16(y1[6], y1[7])};
+      qop[s + 4] = u32x4{pack_f16(y2[0], y2[1]), pack_f16(y2[2], y2[3]), pack_f16(y2[4], y2[5]),
+                         pack_f16(y2[6], y2[7])};
       float* r1 = stg + 16 * s + 8 * hf;
       float* r2 = r1 + 64;
       *reinterpret_cast<float4*>(r1) = make_float4(y1[0], y1[1], y1[2], y1[3]);
@@ -546,32 +487,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       *reinterpret_cast<float4*>(r2) = make_float4(y2[0], y2[1], y2[2], y2[3]);
       *reinterpret_cast<float4*>(r2 + 4) = make_float4(y2[4], y2[5], y2[6], y2[7]);
     }
-    if (tid < 32) {
-      const uint32_t w = (uint32_t)args.sel[g * kSelStride + kSelPerm + tid];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_qperm[4 * tid + e] = (uint8_t)(w >> (8 * e));
-    }
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      uint32_t w4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w4[e] = pack_f16(stg[s_qperm[16 * s + 8 * hf + 2 * e]], stg[s_qperm[16 * s + 8 * hf + 2 * e + 1]]);
-      qop[s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-    }
-    {
-      const uint32_t mask = (uint32_t)args.sel[g * kSelStride + kSelMask + hr] >> (8 * hf);
-      uint32_t lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t h;
-        split_f16(stg[s_qperm[16 * hr + 8 * hf + e]], h, lo[e]);
-        if (!((mask >> e) & 1u)) lo[e] = 0u;
-      }
-      qcorh = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-                    lo[6] | (lo[7] << 16)};
-    }
     uint32_t part[8];
 #pragma unroll
     for (int p = 0; p < kSelPairs; ++p) {
@@ -654,9 +570,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     for (int s = 0; s < 8; ++s)
       sacc = mfma_f16(*reinterpret_cast<const u32x4*>(krow + 16 * s), qop[s], sacc);
     const uint16_t* crow = st.kc + ln * KC_LD + 8 * (hf ^ ((ln >> 3) & 1));
-    sacc = mfma_f16(*reinterpret_cast<const u32x4*>(crow), qcor, sacc);
-    // query-side remainders of this head's pairs against the fp16 keys of slice hr
-    return mfma_f16(*reinterpret_cast<const u32x4*>(krow + 16 * hr), qcorh, sacc);
+    return mfma_f16(*reinterpret_cast<const u32x4*>(crow), qcor, sacc);
   };
   auto qk_local = [&](int so) __attribute__((always_inline)) -> f32x16 {
     const Stage& st = *reinterpret_cast<const Stage*>(smem_raw + so);
