@@ -31,8 +31,9 @@
 //     formula with one of two step rotations evaluated once per wave, and the drift
 //     after thousands of steps stays near 1e-12, far below fp32 rounding.  No table is
 //     read, so decode needs no table in the workspace.
-//   * O^T = V^T P^T (v_mfma_f32_16x16x16_bf16): the block's V rows are transposed
-//     through a per-wave LDS tile (pairs of keys packed per 32-bit word).
+//   * O^T = V^T P^T (v_mfma_f32_16x16x16_bf16): the block's V rows go to a per-wave
+//     LDS tile as loaded, and the transposing LDS read (ds_read_b64_tr_b16) hands each
+//     lane four keys of one channel, the V^T operand.
 //   * Online softmax in the base-2 domain with a lazy running max per head.
 //   * Two waves per SIMD (at most 256 registers each) so that one wave's loads are in
 //     flight while the other computes.
@@ -77,6 +78,16 @@ __device__ __forceinline__ void split8(const float* y, u32x4& hi, u32x4& lo) {
 }
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// ds_read_b64_tr_b16 at an address in LDS (p points into a __shared__ array): within each
+// group of 16 lanes, lane i receives element i & 3 of the 8-byte chunks that lanes i/4,
+// 4 + i/4, 8 + i/4 and 12 + i/4 of its group point to (a 4 x 4 transpose of 16-bit
+// elements per 16-lane group).
+__device__ __forceinline__ v4i16 lds_read_tr16(uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_u8*)p);
+}
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
@@ -111,7 +122,7 @@ template <int REP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeBatchArgs a) {
   using namespace dm;
-  // per wave: V^T tile [128 channels][16 keys] (8-byte segments swizzled by row), P^T
+  // per wave: V tile [16 keys][128 channels] (32-byte blocks swizzled by row), P^T
   // rows [16 heads][16 keys], standard query rows [8 heads][128] + one zero row, and
   // the angle row R(n0) of the current block (lane = RoPE pair)
   __shared__ __align__(16) uint16_t s_vt[NWD][D * BK];
@@ -336,7 +347,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   // the lane's share of its row sum (keys 4kq .. 4kq+3 of every block; summed at the end)
   float m_run = -1e30f, l_run = 0.f;
 
-  uint16_t* vt = s_vt[wave];
+  uint8_t* vtb = reinterpret_cast<uint8_t*>(s_vt[wave]);
   // Blocks alternate between two load buffers (no register copy between blocks): block
   // i + 1's loads go out first and stay in flight while block i is scored.
   auto block = [&](int i, const Blk& cur, Blk& nxt) __attribute__((always_inline)) {
@@ -351,23 +362,16 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     uint4 kr4[4];
     stage_k(cur, kr4);
 
-    // ---- V^T tile: keys (2kp, 2kp+1) of channels 64c + 8cg + e, one word each ----------
-    // row dd: four 8-byte segments of 4 keys; segment q sits at q ^ ((dd >> 2) & 3)
+    // ---- V tile, rows as loaded: row = key, 32-byte block b (16 channels) of row r at
+    // position b ^ (r & 7); lane (kp, cg) stores keys 2kp, 2kp+1 x channels 8cg + 64c
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&cur.v[0][c]);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&cur.v[1][c]);
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int dd = 64 * c + 8 * cg + 2 * ww + hh;
-          const uint32_t word = __byte_perm(a0[ww], a1[ww], hh ? 0x7632 : 0x5410);
-          const int seg = (kp >> 1) ^ ((dd >> 2) & 3);
-          *reinterpret_cast<uint32_t*>(vt + dd * BK + 4 * seg + 2 * (kp & 1)) = word;
-        }
+      for (int c = 0; c < 2; ++c) {
+        const int r = 2 * kp + k2, blk = (cg >> 1) + 4 * c;
+        *reinterpret_cast<uint4*>(vtb + 256 * r + 32 * (blk ^ (r & 7)) + 16 * (cg & 1)) =
+            cur.v[k2][c];
       }
-    }
 
     // ---- scores S[h][key] -------------------------------------------------------------
     f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -449,10 +453,12 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     const uint2 pb = make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int d = 16 * db + l16;
-      const int seg = kq ^ ((d >> 2) & 3);
-      const uint2 va = *reinterpret_cast<const uint2*>(vt + d * BK + 4 * seg);
-      oacc[db] = mfma16k16_bf16(va, pb, oacc[db]);
+      // transposing read: lane j of group kq gives 4 channels 16db + 4(j & 3) .. of key
+      // 4kq + j/4, and lane (channel 16db + l16, group kq) receives keys 4kq .. 4kq+3 of
+      // its channel, the V^T operand
+      const int r = 4 * kq + (l16 >> 2);
+      const v4i16 t = lds_read_tr16(vtb + 256 * r + 32 * (db ^ (r & 7)) + 8 * (l16 & 3));
+      oacc[db] = mfma16k16_bf16(__builtin_bit_cast(uint2, t), pb, oacc[db]);
     }
 
     // ---- advance the block angle to this wave's next block --------------------------------
