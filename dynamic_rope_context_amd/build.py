@@ -23,8 +23,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-at
          "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 # Per-source additions.  The prefill kernel's softmax maxima are fmaxf chains over
 # MFMA results; without NaN semantics the compiler drops the canonicalizing moves it
-# puts before each of them (about 5 VALU instructions per 32-key tile and wave).  A NaN
-# in the inputs still reaches the output through the exponentials and PV.
+# puts before each of them (about 5 VALU instructions per 32-key tile and wave).  The
+# compiler may then assume that no value is a NaN: the prefill's result for inputs that
+# hold NaN or infinity is unspecified (finite inputs, the documented domain, are
+# unaffected).
 EXTRA_FLAGS = {"prefill_mfma.hip": ["-fno-honor-nans"]}
 
 

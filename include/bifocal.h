@@ -106,7 +106,8 @@ bf_status rope_apply(void* x, const int32_t* pos, int32_t pos0, int32_t T, int32
  *   dt = BF_BF16: bf16 in/out, bf16/fp16 MFMA with fp32 accumulation; the remote
  *     branch uses fp16 operands plus a hi/lo correction on the 4 RoPE pairs per KV
  *     head with the largest magnitude bound (chosen by a pre-pass over Q and K).
- *     Requires D = 128 and Hq/Hkv in {1, 2, 4, 8}.
+ *     Requires D = 128 and Hq/Hkv in {1, 2, 4, 8}.  Inputs must be finite: for NaN or
+ *     infinity in Q, K or V the outputs are unspecified.
  *   dt = BF_F32: float32 in/out and arithmetic (VALU); D in {64, 128}, any Hq/Hkv.
  *   ws, ws_bytes: workspace (device) of at least
  *     bifocal_workspace_bytes(BF_OP_PREFILL, max_b L_b, T, B, Hq, Hkv, D).  Besides the
