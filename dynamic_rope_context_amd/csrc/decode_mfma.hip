@@ -25,12 +25,13 @@
 //     R(n) = R(n0) R(n - n0) with n - n0 < 16.  Each lane of a wave owns one RoPE pair
 //     and holds cos/sin(n0 theta_m) of the wave's current block in fp64, rounded to fp32
 //     per block (the values a precomputed table would hold, to within fp32 rounding);
-//     the 16 offset rows R(d) are built once per workgroup.  Consecutive blocks of a wave lie nsplit*16 keys apart,
-//     so n0 advances by one of two integers (the floor map moves by q or q + 1, with
-//     q = floor(nsplit*16 / G)): the fp64 angle pair advances by the angle-addition
-//     formula with one of two step rotations evaluated once per wave, and the drift
-//     after thousands of steps stays near 1e-12, far below fp32 rounding.  No table is
-//     read, so decode needs no table in the workspace.
+//     the 16 offset rows R(d) are built once per workgroup, as fp64 powers of R(1).
+//     Consecutive blocks of a wave lie nsplit*16 keys apart, so n0 advances by one of
+//     two integers (the floor map moves by q or q + 1, with q = floor(nsplit*16 / G)):
+//     the fp64 angle pair advances by the angle-addition formula with one of two step
+//     rotations evaluated once per workgroup, and the drift after thousands of steps
+//     stays near 1e-12, far below fp32 rounding.  No table is read, so decode needs no
+//     table in the workspace.
 //   * O^T = V^T P^T (v_mfma_f32_16x16x16_bf16): the block's V rows go to a per-wave
 //     LDS tile as loaded, and the transposing LDS read (ds_read_b64_tr_b16) hands each
 //     lane four keys of one channel, the V^T operand.
@@ -304,7 +305,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     }
   }
 
-  // ---- query operands (A: rows = query heads, lanes l16 >= REP zero) ------------------
+  // ---- query operands (B: columns = query heads, lanes l16 >= REP zero) ---------------
   // lane (head l16, group kq) holds channels 32s + 8kq + e, s = 0..3
   u32x4 qh[4], ql[4];
   {
@@ -373,7 +374,7 @@ decode_mfma_kernel(DecodeBatchArgs a) {
             cur.v[k2][c];
       }
 
-    // ---- scores S[h][key] -------------------------------------------------------------
+    // ---- scores S^T[key][head] ----------------------------------------------------------
     f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
     if (any_remote) {
       const int jkc = min(jk, pos);
