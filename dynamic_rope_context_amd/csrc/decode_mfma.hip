@@ -174,27 +174,23 @@ decode_mfma_kernel(DecodeBatchArgs a) {
   const uint32_t rs = (uint32_t)a.Hkv * D;  // elements between consecutive cache rows
   const uint16_t* kg = (const uint16_t*)a.K + (size_t)b * a.seq_stride + (size_t)g * D;
   const uint16_t* vg = (const uint16_t*)a.V + (size_t)b * a.seq_stride + (size_t)g * D;
-  // Block loads, one block ahead, to registers.  K: load t takes keys 4t .. 4t+3 of the
-  // block, each a whole 256-byte row (lane: key 4t + (lane >> 4), 16-byte chunk
-  // lane & 15), so one load reads four contiguous row segments; loads that give each key
-  // 64 bytes stream about a tenth slower.  The chunks then go through the wave's LDS tile
-  // to the matrix-core layout (chunk c of key r at position c ^ r of its LDS row, which
-  // keeps both the writes and the reads free of bank conflicts).  V: lane (kp, cg) takes
-  // keys 2kp, 2kp+1, channels 8cg .. 8cg+7 and 64 + 8cg .. 64 + 8cg+7, so the eight lanes
-  // of a key cover 128 contiguous bytes per load.  Keys past pos are clamped to pos (their
-  // scores are masked).
-  const int kp = lane & 7, cg = lane >> 3;
+  // Block loads, one block ahead, to registers.  K and V alike: load t takes keys
+  // 4t .. 4t+3 of the block, each a whole 256-byte row (lane: key 4t + (lane >> 4),
+  // 16-byte chunk lane & 15), so one load reads four contiguous row segments; loads that
+  // give each key 64 bytes stream about a tenth slower, and V loads of 128 bytes per key
+  // about 1% slower.  The K chunks then go through the wave's LDS tile to the
+  // matrix-core layout (chunk c of key r at position c ^ r of its LDS row, which keeps
+  // both the writes and the reads free of bank conflicts); the V chunks go to the V tile.
+  // Keys past pos are clamped to pos (their scores are masked).
   struct Blk {
     u32x4 k[4];  // native vectors: plain register moves, no struct copies
-    uint4 v[2][2];
+    u32x4 v[4];
   };
   // Byte offsets of this lane's loads within a block of 16 whole keys (key rows rs
   // elements apart), fixed for the wave
-  uint32_t koff[4], voff[2];
+  uint32_t koff[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) koff[t] = ((4 * t + (lane >> 4)) * rs + 8 * (lane & 15)) * 2u;
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) voff[k2] = ((2 * kp + k2) * rs + 8 * cg) * 2u;
   auto load_blk = [&](int i, Blk& x) __attribute__((always_inline)) {
     const int j0 = jb + (w + i * nsplit) * BK;
     // 64-bit offset of the block (uniform), 32-bit offsets of the lanes within it.  A
@@ -203,27 +199,19 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     const int jbase = min(j0, pos);
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(kg + (size_t)jbase * rs);
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(vg + (size_t)jbase * rs);
-    uint32_t ko[4], vo[2];
+    uint32_t ko[4];
     if (j0 + BK - 1 <= pos) {  // every key of the block exists (all but the last block)
 #pragma unroll
       for (int t = 0; t < 4; ++t) ko[t] = koff[t];
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) vo[k2] = voff[k2];
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         ko[t] = ((uint32_t)(min(j0 + 4 * t + (lane >> 4), pos) - jbase) * rs + 8 * (lane & 15)) * 2u;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-        vo[k2] = ((uint32_t)(min(j0 + 2 * kp + k2, pos) - jbase) * rs + 8 * cg) * 2u;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) x.k[t] = *reinterpret_cast<const u32x4*>(kb + ko[t]);
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        x.v[k2][c] = *reinterpret_cast<const uint4*>(vb + vo[k2] + 128 * c);
+    for (int t = 0; t < 4; ++t) x.v[t] = *reinterpret_cast<const u32x4*>(vb + ko[t]);
   };
   // K of a block through the wave's LDS tile: lane (key l16, group kq), step s =
   // channels 32s + 8kq .. +7 (chunk 4s + kq).  The wave's LDS operations run in order, so
@@ -364,15 +352,14 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     stage_k(cur, kr4);
 
     // ---- V tile, rows as loaded: row = key, 32-byte block b (16 channels) of row r at
-    // position b ^ (r & 7); lane (kp, cg) stores keys 2kp, 2kp+1 x channels 8cg + 64c
+    // position b ^ (r & 7); load t of lane (key 4t + lane/16, chunk lane mod 16) is one
+    // 16-byte half of such a block (conflict-free: a row's 16 chunks cover all banks)
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r = 2 * kp + k2, blk = (cg >> 1) + 4 * c;
-        *reinterpret_cast<uint4*>(vtb + 256 * r + 32 * (blk ^ (r & 7)) + 16 * (cg & 1)) =
-            cur.v[k2][c];
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int r = 4 * t + (lane >> 4), ch = lane & 15;
+      *reinterpret_cast<u32x4*>(vtb + 256 * r + 32 * ((ch >> 1) ^ (r & 7)) + 16 * (ch & 1)) =
+          cur.v[t];
+    }
 
     // ---- scores S^T[key][head] ----------------------------------------------------------
     f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f}, sl = f32x4{0.f, 0.f, 0.f, 0.f};
