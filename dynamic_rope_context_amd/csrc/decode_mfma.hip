@@ -209,9 +209,9 @@ decode_mfma_kernel(DecodeBatchArgs a) {
         ko[t] = ((uint32_t)(min(j0 + 4 * t + (lane >> 4), pos) - jbase) * rs + 8 * (lane & 15)) * 2u;
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) x.k[t] = *reinterpret_cast<const u32x4*>(kb + ko[t]);
+    for (int t = 0; t < 4; ++t) x.k[t] = ld_stream(kb + ko[t]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) x.v[t] = *reinterpret_cast<const u32x4*>(vb + ko[t]);
+    for (int t = 0; t < 4; ++t) x.v[t] = ld_stream(vb + ko[t]);
   };
   // K of a block through the wave's LDS tile: lane (key l16, group kq), step s =
   // channels 32s + 8kq .. +7 (chunk 4s + kq).  The wave's LDS operations run in order, so
