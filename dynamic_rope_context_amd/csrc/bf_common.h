@@ -28,6 +28,10 @@ __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
 __device__ __forceinline__ void st_stream_f32(void* p, f32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
+__device__ __forceinline__ void st_stream2(void* p, uint32_t a, uint32_t b) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2{a, b}, reinterpret_cast<u32x2*>(p));
+}
 
 // ---------------------------------------------------------------------------
 // Position table kept in the workspace.

@@ -94,22 +94,49 @@ __global__ void __launch_bounds__(256) pair_max_zero_kernel(uint32_t* mx, int n)
   if (i < n) mx[i] = 0u;
 }
 
+// Thread (token lane tl, chunk lane cl): chunk ch = 64 blockIdx.x + cl of the H * 8
+// chunks of a token (head ch / 8, pairs 8 (ch % 8) .. +7: two 16-byte streaming loads of
+// the row halves), tokens t0 + tl, t0 + tl + 4, ...  A wave reads 64 consecutive chunks
+// of one token (2 KiB contiguous); the four token lanes meet in LDS before the atomics.
 __global__ void __launch_bounds__(256) pair_max_kernel(const uint16_t* __restrict__ X, int T,
                                                        int H, int tok_per_block,
                                                        uint32_t* __restrict__ mx) {
-  const int hm = blockIdx.x * 256 + threadIdx.x;  // head * 64 + pair
-  if (hm >= H * 64) return;
-  const int h = hm >> 6, m = hm & 63;
+  __shared__ float s_best[4][64][9];
+  const int tl = threadIdx.x >> 6, cl = threadIdx.x & 63;
+  const int ch = blockIdx.x * 64 + cl;
+  const bool live = ch < H * 8;
+  const int h = ch >> 3, c = ch & 7;
   const int t0 = blockIdx.y * tok_per_block;
   const int t1 = min(T, t0 + tok_per_block);
-  float best = 0.f;
-  for (int t = t0; t < t1; ++t) {
-    const uint16_t* row = X + ((size_t)t * H + h) * mf::D;
-    const float a = __uint_as_float((uint32_t)row[m] << 16);
-    const float b = __uint_as_float((uint32_t)row[m + 64] << 16);
-    best = fmaxf(best, a * a + b * b);
+  float best[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    for (int t = t0 + tl; t < t1; t += 4) {
+      const uint16_t* row = X + ((size_t)t * H + h) * mf::D + 8 * c;
+      const u32x4 a = ld_stream(row), b = ld_stream(row + 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __uint_as_float(e & 1 ? a[e >> 1] & 0xffff0000u : a[e >> 1] << 16);
+        const float y = __uint_as_float(e & 1 ? b[e >> 1] & 0xffff0000u : b[e >> 1] << 16);
+        best[e] = fmaxf(best[e], x * x + y * y);
+      }
+    }
   }
-  atomicMax(mx + hm, __float_as_uint(best));  // non-negative floats order as integers
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_best[tl][cl][e] = best[e];
+  __syncthreads();
+  // thread (e, cl) for e < 4 and e + 4: one pair of the chunk each
+  const int cl2 = threadIdx.x & 63, e0 = threadIdx.x >> 6;
+  const int ch2 = blockIdx.x * 64 + cl2;
+  if (ch2 < H * 8) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = e0 + 4 * k;
+      const float m = fmaxf(fmaxf(s_best[0][cl2][e], s_best[1][cl2][e]),
+                            fmaxf(s_best[2][cl2][e], s_best[3][cl2][e]));
+      // non-negative floats order as integers
+      atomicMax(mx + (ch2 >> 3) * 64 + 8 * (ch2 & 7) + e, __float_as_uint(m));
+    }
+  }
 }
 
 // Smallest e >= 0 with sqrt(m) * 2^-e < 2^15, for a maximum squared pair norm m: every
@@ -725,7 +752,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // ---- epilogue: O = O^T / l, LSE ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qi < L) {
-    // O = (V 2^-e_v)^T P^T 2^e_v / l
+    // O = (V 2^-e_v)^T P^T 2^e_v / l, written with streaming stores (read by no later
+    // workgroup: the caches keep the key tiles instead)
     const float inv = __builtin_ldexpf(1.f, args.sel[g * kSelStride + kSelExpV]) / l_tot;
     const size_t orow_off = ((size_t)(start + qi) * Hq + qhead) * D;
     if (args.out_f32) {
@@ -736,8 +764,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = 32 * db + 8 * q4 + 4 * hf;
           const f32x16& o = oacc[db];
-          *reinterpret_cast<float4*>(orow + d) = make_float4(o[4 * q4] * inv, o[4 * q4 + 1] * inv,
-                                                             o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv);
+          st_stream_f32(orow + d, f32x4{o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv,
+                                        o[4 * q4 + 3] * inv});
         }
     } else {
       uint16_t* orow = (uint16_t*)args.O + orow_off;
@@ -747,9 +775,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = 32 * db + 8 * q4 + 4 * hf;
           const f32x16& o = oacc[db];
-          *reinterpret_cast<uint2*>(orow + d) =
-              make_uint2(pack_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
-                         pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
+          st_stream2(orow + d, pack_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
+                     pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
         }
     }
     if (args.lse && hf == 0)
@@ -768,11 +795,11 @@ hipError_t launch_pair_select(const void* Q, const void* K, const void* V, int T
   const int tpb = 256;  // tokens per block
   const int ty = (T + tpb - 1) / tpb;
   if (ty > 0) {
-    hipLaunchKernelGGL(pair_max_kernel, dim3((Hq * 64 + 255) / 256, ty), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pair_max_kernel, dim3((Hq * 8 + 63) / 64, ty), dim3(256), 0, stream,
                        (const uint16_t*)Q, T, Hq, tpb, mx);
-    hipLaunchKernelGGL(pair_max_kernel, dim3((Hkv * 64 + 255) / 256, ty), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pair_max_kernel, dim3((Hkv * 8 + 63) / 64, ty), dim3(256), 0, stream,
                        (const uint16_t*)K, T, Hkv, tpb, mx + Hq * 64);
-    hipLaunchKernelGGL(pair_max_kernel, dim3((Hkv * 64 + 255) / 256, ty), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pair_max_kernel, dim3((Hkv * 8 + 63) / 64, ty), dim3(256), 0, stream,
                        (const uint16_t*)V, T, Hkv, tpb, mx + (Hq + Hkv) * 64);
   }
   hipLaunchKernelGGL(pair_select_kernel, dim3(Hkv), dim3(64), 0, stream, mx,
