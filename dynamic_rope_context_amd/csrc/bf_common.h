@@ -14,23 +14,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming (non-temporal) 16-byte global loads and stores, for data that one call
-// reads or writes once: the cache hierarchy does not keep such lines.  On the decode
-// sweep over the cache and on rope_apply's in-place pass they take 5-7% off the time.
+// reads or writes once, in accesses whose lanes together cover whole cache lines: the
+// cache hierarchy does not keep such lines.  On the decode sweep over the cache and on
+// rope_apply's in-place pass they take 5-7% off the time.  Stores that cover only part
+// of a line stay cached (the L2 merges them; streamed, they reach HBM as partial
+// writes).
 __device__ __forceinline__ u32x4 ld_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ f32x4 ld_stream_f32(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-}
 __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ void st_stream_f32(void* p, f32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
-}
-__device__ __forceinline__ void st_stream2(void* p, uint32_t a, uint32_t b) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  __builtin_nontemporal_store(u32x2{a, b}, reinterpret_cast<u32x2*>(p));
 }
 
 // ---------------------------------------------------------------------------

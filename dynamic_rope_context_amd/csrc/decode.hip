@@ -36,11 +36,11 @@ struct Row<uint16_t> {
   template <int CPL>
   __device__ __forceinline__ static void load(const uint16_t* p, float* out) {
     if constexpr (CPL == 8) {
-      const u32x4 w = ld_stream(p);  // cache rows are read once per step
-      out[0] = bf16_lo(w[0]); out[1] = bf16_hi(w[0]);
-      out[2] = bf16_lo(w[1]); out[3] = bf16_hi(w[1]);
-      out[4] = bf16_lo(w[2]); out[5] = bf16_hi(w[2]);
-      out[6] = bf16_lo(w[3]); out[7] = bf16_hi(w[3]);
+      const uint4 w = *reinterpret_cast<const uint4*>(p);
+      out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+      out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+      out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
+      out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
     } else {
       const uint2 w = *reinterpret_cast<const uint2*>(p);
       out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
@@ -55,8 +55,8 @@ struct Row<float> {
   __device__ __forceinline__ static void load(const float* p, float* out) {
 #pragma unroll
     for (int c = 0; c < CPL; c += 4) {
-      const f32x4 w = ld_stream_f32(p + c);
-      out[c] = w[0]; out[c + 1] = w[1]; out[c + 2] = w[2]; out[c + 3] = w[3];
+      const float4 w = *reinterpret_cast<const float4*>(p + c);
+      out[c] = w.x; out[c + 1] = w.y; out[c + 2] = w.z; out[c + 3] = w.w;
     }
   }
 };

@@ -752,8 +752,9 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // ---- epilogue: O = O^T / l, LSE ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qi < L) {
-    // O = (V 2^-e_v)^T P^T 2^e_v / l, written with streaming stores (read by no later
-    // workgroup: the caches keep the key tiles instead)
+    // O = (V 2^-e_v)^T P^T 2^e_v / l.  Cached stores: each one covers 16 bytes of a row,
+    // and the L2 merges them into whole lines (streaming stores wrote four times the
+    // bytes of O to HBM).
     const float inv = __builtin_ldexpf(1.f, args.sel[g * kSelStride + kSelExpV]) / l_tot;
     const size_t orow_off = ((size_t)(start + qi) * Hq + qhead) * D;
     if (args.out_f32) {
@@ -764,8 +765,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = 32 * db + 8 * q4 + 4 * hf;
           const f32x16& o = oacc[db];
-          st_stream_f32(orow + d, f32x4{o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv,
-                                        o[4 * q4 + 3] * inv});
+          *reinterpret_cast<float4*>(orow + d) = make_float4(o[4 * q4] * inv, o[4 * q4 + 1] * inv,
+                                                             o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv);
         }
     } else {
       uint16_t* orow = (uint16_t*)args.O + orow_off;
@@ -775,8 +776,9 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = 32 * db + 8 * q4 + 4 * hf;
           const f32x16& o = oacc[db];
-          st_stream2(orow + d, pack_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
-                     pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
+          *reinterpret_cast<uint2*>(orow + d) =
+              make_uint2(pack_bf16(o[4 * q4] * inv, o[4 * q4 + 1] * inv),
+                         pack_bf16(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv));
         }
     }
     if (args.lse && hf == 0)

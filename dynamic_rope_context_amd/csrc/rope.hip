@@ -10,8 +10,9 @@
 // Streaming kernel (HBM-bound: every element is read and written once).  A workgroup
 // takes a block of tokens: first the (cos, sin) of each (token, pair) of the block go to
 // LDS (theta_m once per workgroup, one float64 sincos per pair and token, not per head),
-// then each thread rotates 8 consecutive pairs of one (token, head) with 16-byte
-// streaming loads and stores of both halves (non-temporal: 4-5% faster than cached ones).  Head dims whose half is not a multiple of 8 pairs, or rows
+// then each thread rotates 8 consecutive pairs of one (token, head) with 16-byte loads
+// and stores of both halves.  For bf16 they are streaming (non-temporal: 4-5% faster
+// than cached ones); the eight lanes of a head half cover whole 128-byte lines.  Head dims whose half is not a multiple of 8 pairs, or rows
 // that are not 16-byte aligned, take a one-pair-per-thread kernel.
 #include "bf_common.h"
 
@@ -46,14 +47,15 @@ struct Chunk8<uint16_t> {
 template <>
 struct Chunk8<float> {
   __device__ __forceinline__ static void load(const float* p, float* v) {
-    const f32x4 a = ld_stream_f32(p);
-    const f32x4 b = ld_stream_f32(p + 4);
-    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
   __device__ __forceinline__ static void store(float* p, const float* v) {
-    st_stream_f32(p, f32x4{v[0], v[1], v[2], v[3]});
-    st_stream_f32(p + 4, f32x4{v[4], v[5], v[6], v[7]});
+    // cached: each store covers half of a 32-byte run, which the L2 merges
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
   }
 };
 
