@@ -158,6 +158,9 @@ BF16_CASES = [
     ("rep4_g1", 4, 1, (500,), 600, 64, 0),
     ("rep4_wide_window", 8, 2, (2500,), 512, 1000, 4),
     ("rep4_w0_ge_L", 4, 1, (300,), 64, 400, 4),
+    # 3 KV heads, 12 query heads: 24 and 96 eight-pair chunks per token, so the
+    # pair-maximum pre-pass runs partly filled chunk blocks
+    ("rep4_hkv3", 12, 3, (900, 37), 256, 128, 4),
 ]
 
 
