@@ -69,6 +69,7 @@ constexpr int VT_LD = BK;
 // hi/lo operand rows: 32 B = two chunks, chunk h at position h ^ ((key >> 3) & 1).
 constexpr int KC_LD = 16;
 constexpr float kLazy = 8.f;  // allowed growth of the running max before a rescale
+constexpr float kLazySum = 256.f;  // 2^kLazy
 
 struct Stage {
   uint16_t k[K_DMA * 512];  // key operand: remote fp16 or standard bf16, padded rows
@@ -609,10 +610,12 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     return sacc;
   };
 
-  // Online softmax, part 1: masks, tile row max and the lazy rescale.  MK = 1: remote
-  // pass over a straddling tile, keep i - j >= w0.  MK = 2: local pass over a straddling
-  // or diagonal tile, keep 0 <= i - j < w0 (window and causality in one unsigned compare).
-  auto softmax_prep = [&](int v, f32x16& sacc, float c2, auto mk_c) __attribute__((always_inline)) {
+  // Online softmax with a lazy running max m_run (base 2): m_run moves only when a row's
+  // scores pass it by more than kLazy, so probabilities stay at most 2^kLazy.
+  // Masks: MK = 1: remote pass over a straddling tile, keep i - j >= w0.  MK = 2: local
+  // pass over a straddling or diagonal tile, keep 0 <= i - j < w0 (window and causality
+  // in one unsigned compare).
+  auto apply_mask = [&](int v, f32x16& sacc, auto mk_c) __attribute__((always_inline)) {
     constexpr int MK = decltype(mk_c)::value;
     if constexpr (MK != 0) {
       const int kt = vt_kt(v);
@@ -623,6 +626,10 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
         if (drop) sacc[r] = -INFINITY;
       }
     }
+  };
+  // The lazy rule on the tile's row max: a new m_run when the max passes it by more than
+  // kLazy, with the output and row sum rescaled to it.
+  auto rescale = [&](const f32x16& sacc, float c2) __attribute__((always_inline)) {
     float mx = sacc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
@@ -638,24 +645,24 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       m_run = m_new;
     }
   };
-  // Part 2: probabilities in the PV operand layout (fp16, round to nearest even) and the
-  // row-sum update.  The row sum adds the same rounded probabilities that PV multiplies
-  // (two per v_dot2 against (1, 1), fp32 accumulation), so numerator and denominator
-  // agree.
-  auto softmax_exp = [&](const f32x16& sacc, uint32_t* pk, float c2) __attribute__((always_inline)) {
+  // Probabilities against m_run in the PV operand layout (fp16, round to nearest even)
+  // and the sum of this lane's 16 of them.  The row sum adds the same rounded
+  // probabilities that PV multiplies (two per v_dot2 against (1, 1), fp32 accumulation),
+  // so numerator and denominator agree.
+  auto softmax_exp = [&](const f32x16& sacc, uint32_t* pk, float c2) __attribute__((always_inline)) -> float {
     const float mneg = -m_run;
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    float l0 = l_run, l1 = 0.f;
+    float t0 = 0.f, t1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = fast_exp2(__fmaf_rn(sacc[r], c2, mneg));
       const float p1 = fast_exp2(__fmaf_rn(sacc[r + 1], c2, mneg));
       const f16x2 ph = {(_Float16)p0, (_Float16)p1};
       pk[r / 2] = __builtin_bit_cast(uint32_t, ph);
-      float& acc = (r & 2) ? l1 : l0;
+      float& acc = (r & 2) ? t1 : t0;
       acc = __builtin_amdgcn_fdot2(ph, ones, acc, false);
     }
-    l_run = l0 + l1;
+    return t0 + t1;
   };
   // O^T += V^T P^T over the tile's 32 keys.
   auto pv = [&](const uint32_t* pk, int so) __attribute__((always_inline)) {
@@ -693,14 +700,24 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       __attribute__((always_inline)) {
     constexpr bool QKREM = decltype(qkrem_c)::value;  // class of tile v+1's scores
     issue(v + PREF, slot(v + PREF));
-    // Tile v's row max and rescale first, so that tile v+1's score MFMAs and tile v's
-    // exponentials (independent of each other) share one basic block and interleave.
+    // Tile v+1's score MFMAs and tile v's exponentials (independent of each other) share
+    // one basic block and interleave.
     f32x16 sc = s_in;
     const float c2 = v < nr ? c2r : c2l;  // class of tile v (wave-uniform)
-    softmax_prep(v, sc, c2, mk_c);
+    apply_mask(v, sc, mk_c);
     s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
+    // Probabilities against the current m_run first, the row max only when needed: a
+    // lane's probabilities are each at most their sum, so sums of at most 2^kLazy mean
+    // that no score passed m_run by more than kLazy (the lazy rule keeps m_run).  Larger
+    // sums (the first tiles of a row, a rising max) take the rule on the tile's max and
+    // recompute the probabilities.
     uint32_t pk[8];
-    softmax_exp(sc, pk, c2);
+    float t = softmax_exp(sc, pk, c2);
+    if (__ballot(!(t <= kLazySum))) {
+      rescale(sc, c2);
+      t = softmax_exp(sc, pk, c2);
+    }
+    l_run += t;
     pv(pk, slot(v));
     if (v & 1) wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);
   };
