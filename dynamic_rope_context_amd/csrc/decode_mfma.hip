@@ -56,6 +56,7 @@ constexpr int D = 128;
 constexpr int BK = 16;           // keys per block
 constexpr int NWD = 4;           // waves per workgroup (one split each)
 constexpr float kLazy = 8.f;     // allowed growth of the running max before a rescale
+constexpr float kLazySum = 256.f;  // 2^kLazy
 }  // namespace dm
 
 // fp16 hi/lo of 8 consecutive values, packed as two MFMA operands: hi = RNE(y) by the
@@ -417,25 +418,37 @@ decode_mfma_kernel(DecodeBatchArgs a) {
     }
 
     // ---- online softmax of head l16 -------------------------------------------------------
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = max_lane_xor16(max_lane_xor32(mx));  // the head's four key groups
-    const float bm = fmaxf(m_run, mx * c2);
-    const bool need = bm > m_run + kLazy;
-    if (__ballot(need)) {
-      // O^T column l16 is head l16: the lane's own factor
-      const float mn = need ? bm : m_run;
-      const float f = fast_exp2(m_run - mn);
-      l_run *= f;
-      m_run = mn;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[db] *= f;
-    }
+    // Probabilities against the running max first; the head's max only when a lane's
+    // four probabilities sum past 2^kLazy (each is at most the sum, so otherwise no score
+    // passed m_run by more than kLazy and the lazy rule keeps m_run).
     float pr[4];
+    auto probs = [&]() __attribute__((always_inline)) {
+      float t = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[r] = fast_exp2(__fmaf_rn(sc[r], c2, -m_run));
-      l_run += pr[r];
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = fast_exp2(__fmaf_rn(sc[r], c2, -m_run));
+        t += pr[r];
+      }
+      return t;
+    };
+    float tsum = probs();
+    if (__ballot(!(tsum <= kLazySum))) {
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mx = max_lane_xor16(max_lane_xor32(mx));  // the head's four key groups
+      const float bm = fmaxf(m_run, mx * c2);
+      const bool need = bm > m_run + kLazy;
+      if (__ballot(need)) {
+        // O^T column l16 is head l16: the lane's own factor
+        const float mn = need ? bm : m_run;
+        const float f = fast_exp2(m_run - mn);
+        l_run *= f;
+        m_run = mn;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[db] *= f;
+      }
+      tsum = probs();
     }
+    l_run += tsum;
 
     // ---- O^T += V^T P^T (K = the block's 16 keys): P^T is already in operand layout ------
     const uint2 pb = make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
