@@ -556,12 +556,14 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   }
   const uint32_t lane16 = 16 * lane;
   const uint32_t krow_bytes = 2 * krow_stride;
-  auto issue = [&](int v, int so) __attribute__((always_inline)) {
-    v = min(v, nvt - 1);  // past the end: repeat the last tile (keeps the vmcnt count)
+  // REMSRC: the caller knows that tile v is a remote tile before the end (v < nr)
+  auto issue = [&](int v, int so, auto remsrc_c) __attribute__((always_inline)) {
+    constexpr bool REMSRC = decltype(remsrc_c)::value;
+    if (!REMSRC) v = min(v, nvt - 1);  // past the end: repeat the last tile (keeps the vmcnt count)
     const int kt = vt_kt(v);
     uint8_t* st = smem_raw + so;
     const uint8_t* rec = rec_seq + (size_t)kt * kRecBytes;
-    if (v < nr) {
+    if (REMSRC || v < nr) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         if (q == 0 || wave == 0)
@@ -689,17 +691,17 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   if (nr > 0) load_q_remote();
   else load_q_std();
 #pragma unroll
-  for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes);
+  for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes, std::false_type());
   wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);  // tiles 0 .. 2 in LDS
   f32x16 s_cur = nr > 0 ? qk_remote(0) : qk_local(0);
 
   // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
   // so its scores are computed unconditionally and simply unused past the end.  Two
   // score register sets alternate between consecutive tiles (no copy per tile).
-  auto step = [&](int v, const f32x16& s_in, f32x16& s_out, auto qkrem_c, auto mk_c)
-      __attribute__((always_inline)) {
+  auto step = [&](int v, const f32x16& s_in, f32x16& s_out, auto qkrem_c, auto mk_c,
+                  auto remsrc_c) __attribute__((always_inline)) {
     constexpr bool QKREM = decltype(qkrem_c)::value;  // class of tile v+1's scores
-    issue(v + PREF, slot(v + PREF));
+    issue(v + PREF, slot(v + PREF), remsrc_c);
     // Tile v+1's score MFMAs and tile v's exponentials (independent of each other) share
     // one basic block and interleave.
     f32x16 sc = s_in;
@@ -722,13 +724,14 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     if (v & 1) wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);
   };
   f32x16 s_alt;
-  auto run = [&](int& v, int end, auto qkrem_c, auto mk_c) __attribute__((always_inline)) {
+  auto run = [&](int& v, int end, auto qkrem_c, auto mk_c, auto remsrc_c)
+      __attribute__((always_inline)) {
     for (; v + 1 < end; v += 2) {
-      step(v, s_cur, s_alt, qkrem_c, mk_c);
-      step(v + 1, s_alt, s_cur, qkrem_c, mk_c);
+      step(v, s_cur, s_alt, qkrem_c, mk_c, remsrc_c);
+      step(v + 1, s_alt, s_cur, qkrem_c, mk_c, remsrc_c);
     }
     if (v < end) {
-      step(v, s_cur, s_alt, qkrem_c, mk_c);
+      step(v, s_cur, s_alt, qkrem_c, mk_c, remsrc_c);
       s_cur = s_alt;
       ++v;
     }
@@ -747,20 +750,22 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const int v_rem_mask = ktA - r0;                    // first remote tile needing a mask
   int v = 0;
   if (mode == 2) {
-    run(v, nr - 1, kRem(), kLocMask());
+    run(v, nr - 1, kRem(), kLocMask(), std::false_type());
   } else {
-    run(v, min(v_rem_mask, nr - 1), kRem(), kNoMask());
-    run(v, nr - 1, kRem(), kRemMask());
+    // while the tiles issued (v + PREF) are remote, the transfers skip the class test
+    run(v, min(min(v_rem_mask, nr - 1), nr - PREF), kRem(), kNoMask(), std::true_type());
+    run(v, min(v_rem_mask, nr - 1), kRem(), kNoMask(), std::false_type());
+    run(v, nr - 1, kRem(), kRemMask(), std::false_type());
   }
   if (nr > 0) {  // last remote tile: the next scores are local (or past the end)
     load_q_std();
-    if (mode == 2) run(v, v + 1, kLoc(), kLocMask());
-    else if (v >= v_rem_mask) run(v, v + 1, kLoc(), kRemMask());
-    else run(v, v + 1, kLoc(), kNoMask());
+    if (mode == 2) run(v, v + 1, kLoc(), kLocMask(), std::false_type());
+    else if (v >= v_rem_mask) run(v, v + 1, kLoc(), kRemMask(), std::false_type());
+    else run(v, v + 1, kLoc(), kNoMask(), std::false_type());
   }
-  run(v, min(v_loc_plain, nvt), kLoc(), kLocMask());
-  run(v, min(v_diag, nvt), kLoc(), kNoMask());
-  run(v, nvt, kLoc(), kLocMask());
+  run(v, min(v_loc_plain, nvt), kLoc(), kLocMask(), std::false_type());
+  run(v, min(v_diag, nvt), kLoc(), kNoMask(), std::false_type());
+  run(v, nvt, kLoc(), kLocMask(), std::false_type());
   // Transfers issued past the last tile must land before this workgroup's LDS is
   // handed to another one.
   asm volatile("" ::: "memory");
