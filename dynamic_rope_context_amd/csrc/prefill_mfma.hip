@@ -560,15 +560,15 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   auto issue = [&](int v, int so, auto remsrc_c) __attribute__((always_inline)) {
     constexpr bool REMSRC = decltype(remsrc_c)::value;
     if (!REMSRC) v = min(v, nvt - 1);  // past the end: repeat the last tile (keeps the vmcnt count)
-    const int kt = vt_kt(v);
+    const int kt = REMSRC ? r0 + v : vt_kt(v);
     uint8_t* st = smem_raw + so;
     const uint8_t* rec = rec_seq + (size_t)kt * kRecBytes;
     if (REMSRC || v < nr) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        if (q == 0 || wave == 0)
-          dma16_at(rec, krec_off[q], st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
-      if (wave == 0) dma16_at(rec, kRecKr + lane16, st + offsetof(Stage, kc));
+      dma16_at(rec, krec_off[0], st + offsetof(Stage, k) + 1024 * wave);
+      if (wave == 0) {  // the ninth key-operand KiB and the hi/lo correction rows
+        dma16_at(rec, krec_off[1], st + offsetof(Stage, k) + 1024 * 8);
+        dma16_at(rec, kRecKr + lane16, st + offsetof(Stage, kc));
+      }
     } else {
       const uint8_t* kb = reinterpret_cast<const uint8_t*>(kseq);
 #pragma unroll
@@ -705,7 +705,8 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     // Tile v+1's score MFMAs and tile v's exponentials (independent of each other) share
     // one basic block and interleave.
     f32x16 sc = s_in;
-    const float c2 = v < nr ? c2r : c2l;  // class of tile v (wave-uniform)
+    // class of tile v (wave-uniform; remote wherever the issued tiles are)
+    const float c2 = decltype(remsrc_c)::value || v < nr ? c2r : c2l;
     apply_mask(v, sc, mk_c);
     s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
     // Probabilities against the current m_run first, the row max only when needed: a
@@ -715,7 +716,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
     // recompute the probabilities.
     uint32_t pk[8];
     float t = softmax_exp(sc, pk, c2);
-    if (__ballot(!(t <= kLazySum))) {
+    if (__builtin_expect(__ballot(!(t <= kLazySum)) != 0, 0)) {
       rescale(sc, c2);
       t = softmax_exp(sc, pk, c2);
     }
