@@ -391,6 +391,17 @@ __device__ __forceinline__ void wait_vm_barrier_w(int wave) {
   asm volatile("" ::: "memory");
 }
 
+// The same with the wave's role known at compile time.
+template <int N0, int N, bool W0>
+__device__ __forceinline__ void wait_vm_barrier_s() {
+  static_assert(N0 >= 0 && N0 < 64 && N >= 0 && N < 64, "vmcnt range");
+  constexpr int M = W0 ? N0 : N;
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((M & 15) | (7 << 4) | ((M >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int REP>
 __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   using namespace mf;
@@ -557,15 +568,18 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   const uint32_t lane16 = 16 * lane;
   const uint32_t krow_bytes = 2 * krow_stride;
   // REMSRC: the caller knows that tile v is a remote tile before the end (v < nr)
-  auto issue = [&](int v, int so, auto remsrc_c) __attribute__((always_inline)) {
+  // W0: the caller is wave 0, which also moves the ninth key-operand KiB and the hi/lo
+  // correction rows
+  auto issue = [&](int v, int so, auto remsrc_c, auto w0_c) __attribute__((always_inline)) {
     constexpr bool REMSRC = decltype(remsrc_c)::value;
+    constexpr bool W0 = decltype(w0_c)::value;
     if (!REMSRC) v = min(v, nvt - 1);  // past the end: repeat the last tile (keeps the vmcnt count)
     const int kt = REMSRC ? r0 + v : vt_kt(v);
     uint8_t* st = smem_raw + so;
     const uint8_t* rec = rec_seq + (size_t)kt * kRecBytes;
     if (REMSRC || v < nr) {
       dma16_at(rec, krec_off[0], st + offsetof(Stage, k) + 1024 * wave);
-      if (wave == 0) {  // the ninth key-operand KiB and the hi/lo correction rows
+      if constexpr (W0) {
         dma16_at(rec, krec_off[1], st + offsetof(Stage, k) + 1024 * 8);
         dma16_at(rec, kRecKr + lane16, st + offsetof(Stage, kc));
       }
@@ -573,7 +587,7 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
       const uint8_t* kb = reinterpret_cast<const uint8_t*>(kseq);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        if (q == 0 || wave == 0) {
+        if (q == 0 || W0) {
           const uint32_t j = min((uint32_t)(kt * BK) + krow_r[q], (uint32_t)(L - 1));
           dma16_at(kb, j * krow_bytes + kcol_b[q], st + offsetof(Stage, k) + 1024 * (q == 0 ? wave : 8));
         }
@@ -688,85 +702,91 @@ __global__ void __launch_bounds__(512) prefill_mfma_kernel(PrefillArgs args) {
   // slot of tile v-2, whose last reader (iteration v-2) is behind a barrier.
   constexpr int kVmAhead = 2 * (PREF - 3);    // waves 1..7: two transfers per tile
   constexpr int kVmAhead0 = 3 * (PREF - 3);   // wave 0: three (local tile) or four
-  if (nr > 0) load_q_remote();
-  else load_q_std();
-#pragma unroll
-  for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes, std::false_type());
-  wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);  // tiles 0 .. 2 in LDS
-  f32x16 s_cur = nr > 0 ? qk_remote(0) : qk_local(0);
+  // The tile walk, compiled once for wave 0 and once for the other waves (wave 0 moves
+  // more per tile), so that no transfer or wait tests the wave.
+  auto walk = [&](auto w0_c) __attribute__((always_inline)) {
+    if (nr > 0) load_q_remote();
+    else load_q_std();
+  #pragma unroll
+    for (int u = 0; u < PREF; ++u) issue(u, u * kStageBytes, std::false_type(), w0_c);
+    wait_vm_barrier_s<kVmAhead0, kVmAhead, decltype(w0_c)::value>();  // tiles 0 .. 2 in LDS
+    f32x16 s_cur = nr > 0 ? qk_remote(0) : qk_local(0);
 
-  // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
-  // so its scores are computed unconditionally and simply unused past the end.  Two
-  // score register sets alternate between consecutive tiles (no copy per tile).
-  auto step = [&](int v, const f32x16& s_in, f32x16& s_out, auto qkrem_c, auto mk_c,
-                  auto remsrc_c) __attribute__((always_inline)) {
-    constexpr bool QKREM = decltype(qkrem_c)::value;  // class of tile v+1's scores
-    issue(v + PREF, slot(v + PREF), remsrc_c);
-    // Tile v+1's score MFMAs and tile v's exponentials (independent of each other) share
-    // one basic block and interleave.
-    f32x16 sc = s_in;
-    // class of tile v (wave-uniform; remote wherever the issued tiles are)
-    const float c2 = decltype(remsrc_c)::value || v < nr ? c2r : c2l;
-    apply_mask(v, sc, mk_c);
-    s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
-    // Probabilities against the current m_run first, the row max only when needed: a
-    // lane's probabilities are each at most their sum, so sums of at most 2^kLazy mean
-    // that no score passed m_run by more than kLazy (the lazy rule keeps m_run).  Larger
-    // sums (the first tiles of a row, a rising max) take the rule on the tile's max and
-    // recompute the probabilities.
-    uint32_t pk[8];
-    float t = softmax_exp(sc, pk, c2);
-    if (__builtin_expect(__ballot(!(t <= kLazySum)) != 0, 0)) {
-      rescale(sc, c2);
-      t = softmax_exp(sc, pk, c2);
+    // Tile v+1 always has an LDS slot holding valid data (issue() repeats the last tile),
+    // so its scores are computed unconditionally and simply unused past the end.  Two
+    // score register sets alternate between consecutive tiles (no copy per tile).
+    auto step = [&](int v, const f32x16& s_in, f32x16& s_out, auto qkrem_c, auto mk_c,
+                    auto remsrc_c) __attribute__((always_inline)) {
+      constexpr bool QKREM = decltype(qkrem_c)::value;  // class of tile v+1's scores
+      issue(v + PREF, slot(v + PREF), remsrc_c, w0_c);
+      // Tile v+1's score MFMAs and tile v's exponentials (independent of each other) share
+      // one basic block and interleave.
+      f32x16 sc = s_in;
+      // class of tile v (wave-uniform; remote wherever the issued tiles are)
+      const float c2 = decltype(remsrc_c)::value || v < nr ? c2r : c2l;
+      apply_mask(v, sc, mk_c);
+      s_out = QKREM ? qk_remote(slot(v + 1)) : qk_local(slot(v + 1));
+      // Probabilities against the current m_run first, the row max only when needed: a
+      // lane's probabilities are each at most their sum, so sums of at most 2^kLazy mean
+      // that no score passed m_run by more than kLazy (the lazy rule keeps m_run).  Larger
+      // sums (the first tiles of a row, a rising max) take the rule on the tile's max and
+      // recompute the probabilities.
+      uint32_t pk[8];
+      float t = softmax_exp(sc, pk, c2);
+      if (__builtin_expect(__ballot(!(t <= kLazySum)) != 0, 0)) {
+        rescale(sc, c2);
+        t = softmax_exp(sc, pk, c2);
+      }
+      l_run += t;
+      pv(pk, slot(v));
+      if (v & 1) wait_vm_barrier_s<kVmAhead0, kVmAhead, decltype(w0_c)::value>();
+    };
+    f32x16 s_alt;
+    auto run = [&](int& v, int end, auto qkrem_c, auto mk_c, auto remsrc_c)
+        __attribute__((always_inline)) {
+      for (; v + 1 < end; v += 2) {
+        step(v, s_cur, s_alt, qkrem_c, mk_c, remsrc_c);
+        step(v + 1, s_alt, s_cur, qkrem_c, mk_c, remsrc_c);
+      }
+      if (v < end) {
+        step(v, s_cur, s_alt, qkrem_c, mk_c, remsrc_c);
+        s_cur = s_alt;
+        ++v;
+      }
+    };
+    using kRem = std::true_type;
+    using kLoc = std::false_type;
+    using kNoMask = std::integral_constant<int, 0>;
+    using kRemMask = std::integral_constant<int, 1>;
+    using kLocMask = std::integral_constant<int, 2>;
+    // Phases of the virtual-tile walk (each loop body is specialised):
+    //   remote unmasked [0, ktA) | remote straddling [ktA, ktB) | local straddling
+    //   | local unmasked | local diagonal; the last remote tile switches the query operand.
+    const int kt_diag = i0 >= BK - 1 ? (i0 - (BK - 1)) / BK + 1 : 0;  // first diagonal tile
+    const int v_loc_plain = nr + (ktB - ktA);           // first local tile past the window edge
+    const int v_diag = nr + (max(kt_diag, ktA) - ktA);  // first local tile needing causality
+    const int v_rem_mask = ktA - r0;                    // first remote tile needing a mask
+    int v = 0;
+    if (mode == 2) {
+      run(v, nr - 1, kRem(), kLocMask(), std::false_type());
+    } else {
+      // while the tiles issued (v + PREF) are remote, the transfers skip the class test
+      run(v, min(min(v_rem_mask, nr - 1), nr - PREF), kRem(), kNoMask(), std::true_type());
+      run(v, min(v_rem_mask, nr - 1), kRem(), kNoMask(), std::false_type());
+      run(v, nr - 1, kRem(), kRemMask(), std::false_type());
     }
-    l_run += t;
-    pv(pk, slot(v));
-    if (v & 1) wait_vm_barrier_w<kVmAhead0, kVmAhead>(wave);
+    if (nr > 0) {  // last remote tile: the next scores are local (or past the end)
+      load_q_std();
+      if (mode == 2) run(v, v + 1, kLoc(), kLocMask(), std::false_type());
+      else if (v >= v_rem_mask) run(v, v + 1, kLoc(), kRemMask(), std::false_type());
+      else run(v, v + 1, kLoc(), kNoMask(), std::false_type());
+    }
+    run(v, min(v_loc_plain, nvt), kLoc(), kLocMask(), std::false_type());
+    run(v, min(v_diag, nvt), kLoc(), kNoMask(), std::false_type());
+    run(v, nvt, kLoc(), kLocMask(), std::false_type());
   };
-  f32x16 s_alt;
-  auto run = [&](int& v, int end, auto qkrem_c, auto mk_c, auto remsrc_c)
-      __attribute__((always_inline)) {
-    for (; v + 1 < end; v += 2) {
-      step(v, s_cur, s_alt, qkrem_c, mk_c, remsrc_c);
-      step(v + 1, s_alt, s_cur, qkrem_c, mk_c, remsrc_c);
-    }
-    if (v < end) {
-      step(v, s_cur, s_alt, qkrem_c, mk_c, remsrc_c);
-      s_cur = s_alt;
-      ++v;
-    }
-  };
-  using kRem = std::true_type;
-  using kLoc = std::false_type;
-  using kNoMask = std::integral_constant<int, 0>;
-  using kRemMask = std::integral_constant<int, 1>;
-  using kLocMask = std::integral_constant<int, 2>;
-  // Phases of the virtual-tile walk (each loop body is specialised):
-  //   remote unmasked [0, ktA) | remote straddling [ktA, ktB) | local straddling
-  //   | local unmasked | local diagonal; the last remote tile switches the query operand.
-  const int kt_diag = i0 >= BK - 1 ? (i0 - (BK - 1)) / BK + 1 : 0;  // first diagonal tile
-  const int v_loc_plain = nr + (ktB - ktA);           // first local tile past the window edge
-  const int v_diag = nr + (max(kt_diag, ktA) - ktA);  // first local tile needing causality
-  const int v_rem_mask = ktA - r0;                    // first remote tile needing a mask
-  int v = 0;
-  if (mode == 2) {
-    run(v, nr - 1, kRem(), kLocMask(), std::false_type());
-  } else {
-    // while the tiles issued (v + PREF) are remote, the transfers skip the class test
-    run(v, min(min(v_rem_mask, nr - 1), nr - PREF), kRem(), kNoMask(), std::true_type());
-    run(v, min(v_rem_mask, nr - 1), kRem(), kNoMask(), std::false_type());
-    run(v, nr - 1, kRem(), kRemMask(), std::false_type());
-  }
-  if (nr > 0) {  // last remote tile: the next scores are local (or past the end)
-    load_q_std();
-    if (mode == 2) run(v, v + 1, kLoc(), kLocMask(), std::false_type());
-    else if (v >= v_rem_mask) run(v, v + 1, kLoc(), kRemMask(), std::false_type());
-    else run(v, v + 1, kLoc(), kNoMask(), std::false_type());
-  }
-  run(v, min(v_loc_plain, nvt), kLoc(), kLocMask(), std::false_type());
-  run(v, min(v_diag, nvt), kLoc(), kNoMask(), std::false_type());
-  run(v, nvt, kLoc(), kLocMask(), std::false_type());
+  if (wave == 0) walk(std::true_type());
+  else walk(std::false_type());
   // Transfers issued past the last tile must land before this workgroup's LDS is
   // handed to another one.
   asm volatile("" ::: "memory");
