@@ -62,6 +62,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# queue_primed: every timed region starts with one untimed call enqueued just before its
+# start event.  After the synchronize that precedes it the GPU is idle, so without that
+# call the start event would also time the host's submission of the first timed call
+# (Python, binding, launch: about 0.1 ms, i.e. about 20 us per call over the five
+# rope_apply calls and 0.3-1 us per decode step).  With it, the start event completes when
+# the priming call's kernels do, and the timed calls are already queued behind it: the
+# region holds exactly the timed calls, back to back, as in a serving loop.
+
+
 @contextlib.contextmanager
 def quiet_host():
     """A timed region without Python's cyclic garbage collector: a full collection after
@@ -181,6 +190,7 @@ def bench_prefill(bf, torch, W, steps, warmup, w0=None, three_pass=False,
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     with quiet_host():
+        call()  # primes the queue (see queue_primed)
         ev[0].record(stream)
         for i in range(steps):
             call()
@@ -222,6 +232,7 @@ def bench_rope_apply(bf, torch, W, steps, warmup):
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with quiet_host():
+        bf.rope_apply(x, w.theta)  # primes the queue (see queue_primed)
         e0.record(stream)
         for _ in range(steps):
             bf.rope_apply(x, w.theta)
@@ -262,6 +273,8 @@ def bench_decode(bf, torch, W, passes, warmup, w0=None):
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with quiet_host():
+        bf.bifocal_decode(q[-1], k, v, int(positions[-1]), w.w0, w.w_pretrained, w.theta,
+                          out=o, lse=lse, workspace=ws)  # primes the queue (see queue_primed)
         e0.record(stream)
         for _ in range(passes):
             one_pass()
@@ -300,6 +313,8 @@ def bench_decode_batch(bf, torch, W, passes, warmup, B=8, S=16384):
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with quiet_host():
+        bf.bifocal_decode_batch(q, k, v, positions, w.w0, w.w_pretrained, w.theta, out=o,
+                                lse=lse, workspace=ws)  # primes the queue (see queue_primed)
         e0.record(stream)
         for _ in range(passes):
             one_pass()
