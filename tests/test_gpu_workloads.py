@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as W
-from oracle.bifocal_ref import bifocal_decode_ref, bifocal_rows, group_size
+from oracle.bifocal_ref import bifocal_decode_ref, bifocal_rows, group_size, rope_apply_ref
 from helpers import (BF16_TOL, decode_inputs, errors, ie_conditioning, prefill_inputs,
                      std_query, within)
 
@@ -168,3 +168,30 @@ def test_qwen3_8b_decode_across_boundary(bf):
         err = errors(o[k].float().cpu().numpy(), Or, lse[k].cpu().numpy(), Lr)
         say(f"batched pos={pos} G={group_size(pos + 1, w.w_pretrained)} {err}")
         assert within(err, BF16_TOL), err
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_rope_apply_qwen3_4b_128k_query(bf, G):
+    # rope_apply in place on the 128K workload's query tensor [131072, 32, 128] bf16, the
+    # launch the benchmark times (G = 1: standard RoPE at positions 0 .. T-1; G = 4: the
+    # aliased positions of this length), checked on up to 512 sampled tokens (the first and last 64) x all heads
+    w = W.get("qwen3_4b_128k")
+    T = w.total_tokens
+    q, _, _ = W.raw_inputs_torch(w, "cuda")
+    rng = np.random.default_rng(w.seed + 17)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T),
+                                     rng.integers(64, T - 64, size=384)]))
+    idx = torch.from_numpy(rows.astype(np.int64)).cuda()
+    x = q.index_select(0, idx).float().cpu().numpy()  # the exact bf16 inputs of the rows
+    say(f"rope_apply 128K query tensor G={G}: {len(rows)} sampled tokens x {w.Hq} heads")
+    bf.rope_apply(q, w.theta, G=G)
+    torch.cuda.synchronize()
+    got = q.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    exact = rope_apply_ref(x, rows, w.theta, G)
+    D = w.D
+    x64 = x.astype(np.float64)
+    mag = np.abs(x64[..., :D // 2]) + np.abs(x64[..., D // 2:])
+    mag = np.concatenate([mag, mag], axis=-1)
+    # one bf16 rounding of a float32 rotation, as in the small rope_apply tests
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
+    assert np.all(np.abs(got - exact) <= ulp + 4 * 2.0 ** -24 * mag)
