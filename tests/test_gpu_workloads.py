@@ -11,7 +11,7 @@ import torch
 import workloads as W
 from oracle.bifocal_ref import bifocal_decode_ref, bifocal_rows, group_size, rope_apply_ref
 from helpers import (BF16_TOL, decode_inputs, errors, ie_conditioning, prefill_inputs,
-                     std_query, within)
+                     std_query, std_rope_local, to_dtype, within)
 
 pytestmark = pytest.mark.gpu
 
@@ -195,3 +195,28 @@ def test_rope_apply_qwen3_4b_128k_query(bf, G):
     # one bf16 rounding of a float32 rotation, as in the small rope_apply tests
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
     assert np.all(np.abs(got - exact) <= ulp + 4 * 2.0 ** -24 * mag)
+
+
+def test_decode_batch_8x16k(bf):
+    # the batched decode the benchmark times: 8 sequences of the 128K decode layer's
+    # shape, each with its own 16384-row cache (the 128K workload's cache rows cut into
+    # 8 sequences, standard RoPE at each sequence's own positions), all queries at
+    # position 16383, in one bifocal_decode_batch call; every sequence against the oracle
+    w = W.get("qwen3_8b_decode_128k")
+    B, S = 8, 16384
+    q_raw, k_raw, v_raw = W.raw_decode_inputs(w, S=B * S)
+    cu = [b * S for b in range(B + 1)]
+    say("batched decode 8 x 16K: building the caches on the CPU")
+    Kc = to_dtype(std_rope_local(k_raw, cu, w.theta), "bf16").reshape(B, S, w.Hkv, w.D)
+    Vc = to_dtype(v_raw, "bf16").reshape(B, S, w.Hkv, w.D)
+    qb = np.stack([std_query(q_raw[b], S - 1, w.theta, "bf16") for b in range(B)])
+    positions = [S - 1] * B
+    ws = bf.Workspace.for_op(bf.OP_DECODE, S, w.Hq, w.Hkv, w.D, num_seqs=B)
+    o, lse = bf.bifocal_decode_batch(dev(qb), dev(Kc), dev(Vc), positions, w.w0, w.w_pretrained,
+                                     w.theta, workspace=ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        Or, Lr = bifocal_decode_ref(qb[b], Kc[b], Vc[b], S - 1, w.w0, w.w_pretrained, w.theta)
+        err = errors(o[b].float().cpu().numpy(), Or, lse[b].cpu().numpy(), Lr)
+        say(f"batched sequence {b} pos={S - 1} G={group_size(S, w.w_pretrained)} {err}")
+        assert within(err, BF16_TOL), err
