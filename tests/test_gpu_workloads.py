@@ -34,8 +34,11 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
 
 
-def _prefill_case(bf, name, n_uniform, ie=False, variant="bifocal", min_rows=512):
+def _prefill_case(bf, name, n_uniform, ie=False, variant="bifocal", min_rows=512, w0=None):
     w = W.get(name)
+    if w0 is not None:  # another window on the same inputs (w0 >= L: every pair local)
+        import dataclasses
+        w = dataclasses.replace(w, w0=w0)
     say(f"{name}: building inputs on the CPU")
     Q, K, V, cu = prefill_inputs(w)
     say(f"{name}: GPU prefill" + (" (three-pass inclusion-exclusion form)" if ie else "")
@@ -103,6 +106,12 @@ def test_qwen3_4b_128k_interp_variant(bf):
     _prefill_case(bf, "qwen3_4b_128k", 100, variant="interp", min_rows=128)
 
 
+def test_qwen3_4b_128k_vanilla_mode(bf):
+    # the benchmark's vanilla comparator: the same call with w0 = L (every pair local,
+    # i.e. causal attention with standard RoPE)
+    _prefill_case(bf, "qwen3_4b_128k", 100, min_rows=128, w0=131072)
+
+
 def test_qwen3_4b_128k_three_pass(bf):
     # the pages' literal form (three passes merged by their LSEs) at full size
     _prefill_case(bf, "qwen3_4b_128k", 100, ie=True, min_rows=128)
@@ -128,6 +137,27 @@ def test_qwen3_8b_decode_128k(bf):
                 f" {err}")
             assert within(err, BF16_TOL), err
     torch.cuda.synchronize()
+
+
+def test_qwen3_8b_decode_128k_vanilla_mode(bf):
+    # the benchmark's vanilla decode comparator: w0 past the position (every key local)
+    import dataclasses
+    w = dataclasses.replace(W.get("qwen3_8b_decode_128k"), w0=1 << 20)
+    say("vanilla decode: building the cache on the CPU")
+    q_raw, Kc, Vc = decode_inputs(w)
+    Kd, Vd = dev(Kc), dev(Vc)
+    ws = bf.Workspace.for_op(bf.OP_DECODE, w.cache_len, w.Hq, w.Hkv, w.D)
+    positions = w.decode_positions()
+    for step in (0, len(positions) - 1):
+        pos = int(positions[step])
+        q = std_query(q_raw[step], pos, w.theta, "bf16")
+        o, lse = bf.bifocal_decode(dev(q), Kd, Vd, pos, w.w0, w.w_pretrained, w.theta,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        Or, Lr = bifocal_decode_ref(q, Kc, Vc, pos, w.w0, w.w_pretrained, w.theta)
+        err = errors(o.float().cpu().numpy(), Or, lse.cpu().numpy(), Lr)
+        say(f"vanilla decode step {step} pos={pos} {err}")
+        assert within(err, BF16_TOL), err
 
 
 def test_qwen3_8b_decode_across_boundary(bf):
